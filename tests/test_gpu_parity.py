@@ -1,0 +1,88 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded workloads.
+
+Tolerances (relative L2 over each returned tensor): 1e-4 for fp32 inputs,
+1e-2 for bf16 inputs (the spec bar). Sizes span several 64-token chunks,
+ragged chunk tails, forks in the middle of chunks, nested forks, tree chunks
+of every size up to 64 and several heads.
+"""
+import numpy as np
+import pytest
+
+from tree_forked_gated_amd import workloads as W
+
+from gpu_helpers import f64, oracle_ref, rel_l2, run_forward, say, tol
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(wl, name, dv_tile=0, pseudo=True):
+    leaves = W.leaves_of(wl.parent)
+    rows = wl.state_rows if wl.state_rows.size else leaves
+    say(f"parity {name}: T={wl.T} H={wl.H} Dk={wl.Dk} Dv={wl.Dv} dtype={wl.dtype} dv_tile={dv_tile}")
+    res, _ = run_forward(wl, keep_pseudo=pseudo, state_rows=rows, dv_tile=dv_tile)
+    ref = oracle_ref(wl, state_rows=rows)
+    ref_out = ref["out"] if wl.out_rows is None else ref["out"][wl.out_rows]
+    errs = {"out": rel_l2(f64(res.out), ref_out), "state": rel_l2(f64(res.state), ref["state"])}
+    if pseudo:
+        errs["pseudo_v"] = rel_l2(f64(res.pseudo_v), ref["pseudo_v"])
+    say(f"  rel-L2 {errs}")
+    for k, e in errs.items():
+        assert e <= tol(wl), (name, k, e)
+    return res, ref
+
+
+def test_config0_tiny_tree_fp32():
+    wl = W.config0()
+    res, ref = _check(wl, "config0")
+    # the five leaf states of the workload
+    assert res.state.shape[0] == 5
+
+
+@pytest.mark.parametrize("seed,Dk,Dv", [(1, 16, 16), (2, 32, 48), (3, 64, 32), (4, 64, 64), (5, 16, 128)])
+def test_random_fp32(seed, Dk, Dv):
+    wl = W.random_small(seed, n_seq=4, H=2, Dk=Dk, Dv=Dv, dtype="f32", max_len=300)
+    _check(wl, f"random_f32[{seed}]")
+
+
+@pytest.mark.parametrize("seed,Dk,Dv", [(6, 32, 32), (7, 64, 64), (8, 128, 128), (9, 128, 64), (10, 128, 16)])
+def test_random_bf16(seed, Dk, Dv):
+    wl = W.random_small(seed, n_seq=4, H=2, Dk=Dk, Dv=Dv, dtype="bf16", max_len=300)
+    _check(wl, f"random_bf16[{seed}]")
+
+
+def test_chains_bf16():
+    wl = W.config1(n_seq=3, L=333, H=3, D=128)
+    _check(wl, "chains")
+
+
+def test_decision_round_bf16():
+    wl = W.config2(n_req=2, trunk=300, n_branch=5, blen=32, H=2, D=128)
+    _check(wl, "decision")
+
+
+def test_draft_trees_bf16():
+    wl = W.config3(n_seq=8, n_nodes=64, H=2, D=128)
+    _check(wl, "draft")
+
+
+def test_mixed_forest_bf16():
+    wl = W.config4(total=4000, H=2, D=128, trunk_range=(100, 900), branch_count=(1, 12), branch_len=(1, 90))
+    _check(wl, "mixed")
+
+
+@pytest.mark.parametrize("n_nodes", [1, 2, 17, 63, 64])
+def test_tree_chunk_sizes_fp32(n_nodes):
+    wl = W.config3(n_seq=3, n_nodes=n_nodes, H=1, D=16)
+    wl.dtype = "f32"
+    _check(wl, f"tree{n_nodes}")
+
+
+@pytest.mark.parametrize("dv_tile", [16, 32, 64])
+def test_dv_tiles_bitwise_identical(dv_tile):
+    wl = W.random_small(21, n_seq=4, H=2, Dk=128, Dv=128, dtype="bf16", max_len=200)
+    base, _ = run_forward(wl, keep_pseudo=True, state_rows=W.leaves_of(wl.parent), dv_tile=16)
+    say(f"dv tile {dv_tile} vs 16")
+    res, _ = run_forward(wl, keep_pseudo=True, state_rows=W.leaves_of(wl.parent), dv_tile=dv_tile)
+    assert np.array_equal(res.out.view(dtype=base.out.dtype).cpu().float().numpy(), base.out.cpu().float().numpy())
+    assert np.array_equal(res.state.cpu().numpy(), base.state.cpu().numpy())
+    assert np.array_equal(res.pseudo_v.cpu().numpy(), base.pseudo_v.cpu().numpy())

@@ -1,0 +1,99 @@
+"""GPU metadata is bit-exact against the reference planner (oracle/plan.py)."""
+import numpy as np
+import pytest
+
+from oracle import plan as P
+from tree_forked_gated_amd import workloads as W
+
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare(parent, seq_start, **kw):
+    from tree_forked_gated_amd import binding as B
+    ref = P.plan(parent, seq_start, max_forks=kw.get("max_forks"), max_levels=kw.get("max_levels"),
+                 out_rows=kw.get("out_rows"), state_rows=kw.get("state_rows"))
+    got = B.plan(parent, seq_start, **kw)
+    assert tuple(int(x) for x in got["error"]) == tuple(ref["error"]), (got["error"], ref["error"])
+    if ref["error"] != (0, 0):
+        return got, ref
+    assert got["n_seg"] == ref["n_seg"] and got["n_fork"] == ref["n_fork"]
+    for f in ["tok_seq", "depth", "fork_slot"]:
+        assert np.array_equal(got[f], ref[f]), f
+    for f in ["seg_start", "seg_len", "seg_seq", "seg_mode", "seg_entry", "seg_slot", "seg_level"]:
+        assert np.array_equal(got[f], ref[f]), f
+    assert np.array_equal(got["tree_mask"], ref["tree_mask"])
+    # levels: the set of segments of every level (order inside a level is unspecified)
+    ptr = got["level_ptr"]
+    for lv in range(len(got["level_count"])):
+        items = sorted(got["level_items"][ptr[lv]:ptr[lv + 1]].tolist())
+        assert items == np.nonzero(ref["seg_level"] == lv)[0].tolist()
+    return got, ref
+
+
+def test_plan_config0():
+    wl = W.config0()
+    say("plan config0")
+    got, _ = _compare(wl.parent, wl.seq_start)
+    assert got["seg_start"].tolist() == [0, 40, 48, 56, 64]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_plan_random(seed):
+    wl = W.random_small(seed, n_seq=7, H=1, Dk=16, Dv=16, max_len=400)
+    say(f"plan random_small seed={seed} T={wl.T}")
+    _compare(wl.parent, wl.seq_start)
+
+
+def test_plan_draft_trees_and_forests():
+    wl = W.config3(n_seq=16, n_nodes=64, H=1, D=32)
+    say("plan config3 structure")
+    _compare(wl.parent, wl.seq_start)
+    wl = W.config4(total=20000, H=1, D=32)
+    say(f"plan config4-shaped structure T={wl.T}")
+    _compare(wl.parent, wl.seq_start)
+
+
+def test_plan_full_size_structures():
+    for n, kw in [(2, {}), (4, {})]:
+        wl = W.get_config(n, H=1, D=32)
+        say(f"plan full-size structure config{n} T={wl.T}")
+        _compare(wl.parent, wl.seq_start)
+
+
+@pytest.mark.parametrize("case", ["order", "self", "below", "crossseq", "seqstart", "seqlast", "forkcap", "levelcap",
+                                  "rowdup", "rowrange"])
+def test_plan_errors_match(case):
+    wl = W.random_small(11, n_seq=4, H=1, Dk=16, Dv=16, max_len=200)
+    parent = wl.parent.copy()
+    seq = wl.seq_start.copy()
+    kw = {}
+    T = wl.T
+    if case == "order":
+        parent[T - 3] = T - 1
+    elif case == "self":
+        parent[5] = 5
+    elif case == "below":
+        parent[7] = -5
+    elif case == "crossseq":
+        t = int(seq[2]) + 1
+        parent[t] = int(seq[1]) - 1
+    elif case == "seqstart":
+        seq[2] = seq[1] - 1
+    elif case == "seqlast":
+        seq[-1] = T - 1
+    elif case == "forkcap":
+        ref = P.plan(parent, seq)
+        kw = {"max_forks": max(0, ref["n_fork"] - 1), "max_levels": 64}
+    elif case == "levelcap":
+        ref = P.plan(parent, seq)
+        kw = {"max_forks": ref["n_fork"], "max_levels": max(1, ref["n_levels"] - 1)}
+    elif case == "rowdup":
+        kw = {"out_rows": np.array([1, 2, 1], np.int32)}
+    elif case == "rowrange":
+        kw = {"state_rows": np.array([0, T], np.int32)}
+    say(f"plan error case {case}")
+    got, ref = _compare(parent, seq, **kw)
+    if case not in ("forkcap", "levelcap") or ref["error"] != (0, 0):
+        assert ref["error"] != (0, 0)

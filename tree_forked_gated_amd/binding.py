@@ -1,0 +1,345 @@
+"""ctypes binding of libgdn_tree.so (include/gdn_tree.h).
+
+Argument marshalling only: every step of the forward and the commit runs in the
+library's HIP kernels. PyTorch provides device memory and the current stream.
+If the library has not been built, importing this module raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn_tree.so")
+
+GDN_F32, GDN_BF16 = 0, 1
+DEV_ERRORS = {0: "ok", 1: "seq_start", 2: "parent order", 3: "parent in another sequence", 4: "fork capacity",
+              5: "level capacity", 6: "rows", 7: "commit path"}
+CHUNK = 64
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int32), ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32),
+                ("n_seq", ctypes.c_int32), ("dtype", ctypes.c_int32), ("max_forks", ctypes.c_int32),
+                ("max_levels", ctypes.c_int32)]
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("dims", Dims), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("log_gate", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("parent_idx", ctypes.c_void_p),
+                ("seq_start", ctypes.c_void_p), ("init_state", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("out_rows", ctypes.c_void_p), ("n_out", ctypes.c_int32), ("state_out", ctypes.c_void_p),
+                ("state_rows", ctypes.c_void_p), ("n_state", ctypes.c_int32), ("pseudo_v", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("dv_tile", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+class CommitArgs(ctypes.Structure):
+    _fields_ = [("dims", Dims), ("k", ctypes.c_void_p), ("log_gate", ctypes.c_void_p),
+                ("parent_idx", ctypes.c_void_p), ("seq_start", ctypes.c_void_p), ("init_state", ctypes.c_void_p),
+                ("pseudo_v", ctypes.c_void_p), ("n_path", ctypes.c_int32), ("path_ptr", ctypes.c_void_p),
+                ("path_nodes", ctypes.c_void_p), ("path_seq", ctypes.c_void_p), ("out_state", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+_LAYOUT_FIELDS = ["err", "n_seg", "n_fork", "tok_seq", "depth", "fork_slot", "seg_start", "seg_len", "seg_seq",
+                  "seg_mode", "seg_entry", "seg_slot", "seg_level", "level_count", "level_ptr", "level_items",
+                  "tree_mask", "fork_states", "total"]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_size_t) for f in _LAYOUT_FIELDS]
+
+
+EXPORTS = ["gdn_tree_workspace_size", "gdn_tree_plan_layout", "gdn_tree_commit_workspace_size", "gdn_tree_plan",
+           "gdn_tree_forward", "gdn_tree_commit", "gdn_tree_check_error", "gdn_tree_strerror",
+           "gdn_tree_last_error", "gdn_tree_version"]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name in EXPORTS:
+        getattr(lib, name)
+    lib.gdn_tree_strerror.restype = ctypes.c_char_p
+    lib.gdn_tree_last_error.restype = ctypes.c_char_p
+    lib.gdn_tree_commit_workspace_size.restype = ctypes.c_size_t
+    for name in ["gdn_tree_workspace_size", "gdn_tree_plan_layout", "gdn_tree_plan", "gdn_tree_forward",
+                 "gdn_tree_commit", "gdn_tree_check_error", "gdn_tree_version"]:
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+class GdnError(RuntimeError):
+    pass
+
+
+class GdnDeviceError(GdnError):
+    def __init__(self, code, index):
+        super().__init__(f"device error {code} ({DEV_ERRORS.get(code, '?')}) at index {index}")
+        self.code = code
+        self.index = index
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise GdnError(f"{what}: {lib.gdn_tree_strerror(rc).decode()} ({rc}): {lib.gdn_tree_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return GDN_F32
+    if dt == torch.bfloat16:
+        return GDN_BF16
+    raise GdnError(f"unsupported dtype {dt}")
+
+
+# ----------------------------------------------------------------- capacities
+
+def capacities(parent, seq_start) -> dict:
+    """Exact fork-slot and level counts of a tree (host-side, from the same
+    segment rules the device planner applies). A convenience for callers that
+    hold the structure on the host; it synchronises if given device tensors."""
+    parent = np.asarray(parent.cpu() if isinstance(parent, torch.Tensor) else parent, dtype=np.int64)
+    seq_start = np.asarray(seq_start.cpu() if isinstance(seq_start, torch.Tensor) else seq_start, dtype=np.int64)
+    T = parent.shape[0]
+    if T == 0:
+        return {"max_forks": 0, "max_levels": 1}
+    lens = np.diff(seq_start)
+    tok_seq = np.repeat(np.arange(lens.shape[0]), lens)
+    tree_tok = lens[tok_seq] <= CHUNK
+    idx = np.arange(T)
+    start = np.where(tree_tok, idx == seq_start[tok_seq], (parent < 0) | (parent != idx - 1))
+    starts = np.nonzero(start)[0]
+    entry = np.where(tree_tok[starts], -1, parent[starts])
+    forks = np.unique(entry[entry >= 0])
+    seg_of = np.cumsum(start) - 1
+    level = np.zeros(starts.shape[0], dtype=np.int64)
+    for i in np.nonzero(entry >= 0)[0]:
+        level[i] = level[seg_of[entry[i]]] + 1
+    return {"max_forks": int(forks.shape[0]), "max_levels": int(level.max()) + 1 if level.size else 1}
+
+
+# ------------------------------------------------------------------- layouts
+
+def make_dims(T, H, Dk, Dv, n_seq, dtype_code, max_forks, max_levels) -> Dims:
+    return Dims(int(T), int(H), int(Dk), int(Dv), int(n_seq), int(dtype_code), int(max_forks), int(max_levels))
+
+
+def workspace_size(dims: Dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.gdn_tree_workspace_size(ctypes.byref(dims), ctypes.byref(n)), "gdn_tree_workspace_size")
+    return int(n.value)
+
+
+def plan_layout(dims: Dims) -> dict:
+    L = Layout()
+    _check(lib.gdn_tree_plan_layout(ctypes.byref(dims), ctypes.byref(L)), "gdn_tree_plan_layout")
+    return {f: int(getattr(L, f)) for f in _LAYOUT_FIELDS}
+
+
+def alloc_workspace(dims: Dims, device) -> torch.Tensor:
+    return torch.empty(workspace_size(dims), dtype=torch.uint8, device=device)
+
+
+def check_error(workspace: torch.Tensor, stream=None):
+    code = ctypes.c_int32(0)
+    index = ctypes.c_int64(0)
+    _check(lib.gdn_tree_check_error(_ptr(workspace), _stream(stream), ctypes.byref(code), ctypes.byref(index)),
+           "gdn_tree_check_error")
+    return int(code.value), int(index.value)
+
+
+def raise_device_error(workspace: torch.Tensor, stream=None):
+    code, index = check_error(workspace, stream)
+    if code != 0:
+        raise GdnDeviceError(code, index)
+
+
+# ------------------------------------------------------------------- forward
+
+@dataclass
+class ForwardResult:
+    out: torch.Tensor
+    state: torch.Tensor
+    pseudo_v: Optional[torch.Tensor]
+    workspace: torch.Tensor
+
+
+def _fwd_args(q, k, v, log_gate, beta, parent_idx, seq_start, init_state, out, out_rows, state_out, state_rows,
+              pseudo_v, workspace, dims, dv_tile):
+    a = FwdArgs()
+    a.dims = dims
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.log_gate, a.beta = _ptr(log_gate), _ptr(beta)
+    a.parent_idx, a.seq_start = _ptr(parent_idx), _ptr(seq_start)
+    a.init_state = _ptr(init_state)
+    a.out = _ptr(out) if out is not None and out.numel() > 0 else None
+    a.out_rows = _ptr(out_rows)
+    a.n_out = int(out.shape[0]) if out is not None else 0
+    a.state_out = _ptr(state_out) if state_out is not None and state_out.numel() > 0 else None
+    a.state_rows = _ptr(state_rows) if state_rows is not None and state_rows.numel() > 0 else None
+    a.n_state = int(state_rows.numel()) if state_rows is not None else 0
+    a.pseudo_v = _ptr(pseudo_v)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = int(workspace.numel())
+    a.dv_tile = int(dv_tile)
+    a.flags = 0
+    return a
+
+
+def _i32(x, device):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.to(device=device, dtype=torch.int32).contiguous()
+    return torch.as_tensor(np.asarray(x, dtype=np.int32), device=device)
+
+
+def forward(q, k, v, log_gate, beta, parent_idx, seq_start, init_state=None, *, out_rows=None, state_rows=None,
+            keep_pseudo=False, max_forks=None, max_levels=None, dv_tile=0, workspace=None, out=None, state_out=None,
+            pseudo_v=None, stream=None, check=False) -> ForwardResult:
+    """gdn_tree_forward on torch tensors (device, contiguous).
+
+    q, k [T,H,Dk], v [T,H,Dv], log_gate, beta [T,H] in float32 or bfloat16;
+    parent_idx [T] and seq_start [n_seq+1] int32; init_state [n_seq,H,Dv,Dk]
+    float32 or None. Returns out rows (all tokens unless out_rows), states of
+    state_rows, pseudo-values when keep_pseudo, and the workspace (metadata and
+    error word). max_forks / max_levels default to the tree's exact counts,
+    computed on the host (a synchronising convenience)."""
+    device = q.device
+    T, H, Dk = q.shape
+    Dv = v.shape[2]
+    parent_idx = _i32(parent_idx, device)
+    seq_start = _i32(seq_start, device)
+    out_rows = _i32(out_rows, device)
+    state_rows = _i32(state_rows, device)
+    n_seq = seq_start.numel() - 1
+    if max_forks is None or max_levels is None:
+        cap = capacities(parent_idx, seq_start)
+        max_forks = cap["max_forks"] if max_forks is None else max_forks
+        max_levels = cap["max_levels"] if max_levels is None else max_levels
+    dims = make_dims(T, H, Dk, Dv, n_seq, _dtype_code(q.dtype), max_forks, max(1, max_levels))
+    if workspace is None:
+        workspace = alloc_workspace(dims, device)
+    n_out = T if out_rows is None else out_rows.numel()
+    if out is None:
+        out = torch.empty((n_out, H, Dv), dtype=q.dtype, device=device)
+    n_state = 0 if state_rows is None else state_rows.numel()
+    if state_out is None:
+        state_out = torch.empty((n_state, H, Dv, Dk), dtype=torch.float32, device=device)
+    if keep_pseudo and pseudo_v is None:
+        pseudo_v = torch.empty((T, H, Dv), dtype=torch.float32, device=device)
+    a = _fwd_args(q, k, v, log_gate, beta, parent_idx, seq_start, init_state, out, out_rows, state_out, state_rows,
+                  pseudo_v, workspace, dims, dv_tile)
+    _check(lib.gdn_tree_forward(ctypes.byref(a), _stream(stream)), "gdn_tree_forward")
+    if check:
+        raise_device_error(workspace, stream)
+    return ForwardResult(out, state_out, pseudo_v, workspace)
+
+
+def plan(parent_idx, seq_start, *, T=None, H=1, Dk=16, Dv=16, dtype_code=GDN_F32, out_rows=None, state_rows=None,
+         max_forks=None, max_levels=None, device="cuda", stream=None) -> dict:
+    """Run only the metadata kernels and return every table (host numpy)."""
+    parent_idx = _i32(parent_idx, device)
+    seq_start = _i32(seq_start, device)
+    out_rows = _i32(out_rows, device)
+    state_rows = _i32(state_rows, device)
+    T = parent_idx.numel() if T is None else T
+    n_seq = seq_start.numel() - 1
+    if max_forks is None or max_levels is None:
+        try:
+            cap = capacities(parent_idx, seq_start)
+        except Exception:  # malformed structure: any capacity will do, the device reports the error
+            cap = {"max_forks": T, "max_levels": 8}
+        max_forks = cap["max_forks"] if max_forks is None else max_forks
+        max_levels = cap["max_levels"] if max_levels is None else max_levels
+    dims = make_dims(T, H, Dk, Dv, n_seq, dtype_code, max_forks, max(1, max_levels))
+    ws = alloc_workspace(dims, device)
+    a = FwdArgs()
+    a.dims = dims
+    a.parent_idx, a.seq_start = _ptr(parent_idx), _ptr(seq_start)
+    a.out_rows = _ptr(out_rows)
+    a.n_out = T if out_rows is None else out_rows.numel()
+    a.state_rows = _ptr(state_rows)
+    a.n_state = 0 if state_rows is None else state_rows.numel()
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = ws.numel()
+    _check(lib.gdn_tree_plan(ctypes.byref(a), _stream(stream)), "gdn_tree_plan")
+    torch.cuda.synchronize(device)
+    L = plan_layout(dims)
+    host = ws.cpu().numpy()
+
+    def i32(name, n):
+        return host[L[name]:L[name] + 4 * n].view(np.int32).copy()
+
+    word = int(host[L["err"]:L["err"] + 8].view(np.uint64)[0])
+    err = (0, 0) if word == 0xFFFFFFFFFFFFFFFF else (word >> 32, word & 0xFFFFFFFF)
+    n_seg = int(i32("n_seg", 1)[0])
+    n_fork = int(i32("n_fork", 1)[0])
+    ml = dims.max_levels
+    out = {"error": err, "n_seg": n_seg, "n_fork": n_fork, "tok_seq": i32("tok_seq", T), "depth": i32("depth", T),
+           "fork_slot": i32("fork_slot", T), "level_count": i32("level_count", ml),
+           "level_ptr": i32("level_ptr", ml + 1),
+           "tree_mask": host[L["tree_mask"]:L["tree_mask"] + 8 * n_seq * CHUNK].view(np.uint64).reshape(n_seq, CHUNK)
+           .copy()}
+    for f in ["seg_start", "seg_len", "seg_seq", "seg_mode", "seg_entry", "seg_slot", "seg_level", "level_items"]:
+        out[f] = i32(f, T)[:n_seg]
+    return out
+
+
+# -------------------------------------------------------------------- commit
+
+def commit(k, log_gate, parent_idx, seq_start, init_state, pseudo_v, path_ptr, path_nodes, path_seq, *,
+           workspace=None, out_state=None, stream=None, check=False) -> torch.Tensor:
+    """gdn_tree_commit: states after each accepted path (TreeWY Eq. 3)."""
+    device = k.device
+    T, H, Dk = k.shape
+    Dv = pseudo_v.shape[2]
+    parent_idx = _i32(parent_idx, device)
+    seq_start = _i32(seq_start, device)
+    path_ptr = _i32(path_ptr, device)
+    path_nodes = _i32(path_nodes, device)
+    path_seq = _i32(path_seq, device)
+    n_path = path_ptr.numel() - 1
+    if workspace is None:
+        workspace = torch.empty(int(lib.gdn_tree_commit_workspace_size()), dtype=torch.uint8, device=device)
+    if out_state is None:
+        out_state = torch.empty((n_path, H, Dv, Dk), dtype=torch.float32, device=device)
+    a = CommitArgs()
+    a.dims = make_dims(T, H, Dk, Dv, seq_start.numel() - 1, _dtype_code(k.dtype), 0, 1)
+    a.k, a.log_gate = _ptr(k), _ptr(log_gate)
+    a.parent_idx, a.seq_start = _ptr(parent_idx), _ptr(seq_start)
+    a.init_state, a.pseudo_v = _ptr(init_state), _ptr(pseudo_v)
+    a.n_path = n_path
+    a.path_ptr = _ptr(path_ptr)
+    a.path_nodes = _ptr(path_nodes) if path_nodes.numel() else _ptr(path_ptr)
+    a.path_seq = _ptr(path_seq)
+    a.out_state = _ptr(out_state) if out_state.numel() else None
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel()
+    _check(lib.gdn_tree_commit(ctypes.byref(a), _stream(stream)), "gdn_tree_commit")
+    if check:
+        raise_device_error(workspace, stream)
+    return out_state

@@ -1,0 +1,201 @@
+// The C ABI of include/gdn_tree.h: argument checks on the host, then kernel
+// launches on the caller's stream. No allocation, no synchronisation (except
+// gdn_tree_check_error), no state kept between calls.
+#include <stdio.h>
+
+#include <string>
+
+#include "gdn_internal.h"
+
+using namespace gdn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return GDN_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_dims(const gdn_tree_dims* d) {
+  if (!d) return fail(GDN_ERR_NULL, "dims is NULL");
+  if (d->dtype != GDN_F32 && d->dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "dtype must be GDN_F32 or GDN_BF16");
+  if (d->T < 0 || d->T > 0x7fffffffLL) return fail(GDN_ERR_DIMS, "T must be in [0, 2^31)");
+  if (d->H < 1 || d->n_seq < 0) return fail(GDN_ERR_DIMS, "H must be >= 1 and n_seq >= 0");
+  if (d->Dv < 16 || d->Dv > 128 || d->Dv % 16) return fail(GDN_ERR_DIMS, "Dv must be a multiple of 16 in [16, 128]");
+  const bool dk_ok = d->dtype == GDN_BF16 ? (d->Dk == 32 || d->Dk == 64 || d->Dk == 128)
+                                          : (d->Dk == 16 || d->Dk == 32 || d->Dk == 64);
+  if (!dk_ok) return fail(GDN_ERR_DIMS, "Dk must be 32, 64 or 128 (bf16) or 16, 32 or 64 (fp32)");
+  if (d->max_forks < 0 || d->max_levels < 1 || d->max_levels > 4096)
+    return fail(GDN_ERR_DIMS, "max_forks must be >= 0 and max_levels in [1, 4096]");
+  return GDN_OK;
+}
+
+// Columns of Dv per workgroup: enough items to give every CU one, widest tile otherwise.
+int choose_dv_tile(const gdn_tree_dims& d) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  }
+  const long long units = (long long)(d.n_seq > 0 ? d.n_seq : 1) * d.H;
+  const int max_bv = d.dtype == GDN_BF16 ? 64 : 32;
+  for (int bv = max_bv; bv >= 16; bv >>= 1) {
+    if (d.Dv % bv) continue;
+    if (units * (d.Dv / bv) >= cus || bv == 16) return bv;
+  }
+  return 16;
+}
+
+int check_fwd(const gdn_tree_fwd_args* a, bool walk, LayoutFull* L) {
+  if (!a) return fail(GDN_ERR_NULL, "args is NULL");
+  int rc = check_dims(&a->dims);
+  if (rc) return rc;
+  const gdn_tree_dims& d = a->dims;
+  if (!a->parent_idx || !a->seq_start || !a->workspace) return fail(GDN_ERR_NULL, "parent_idx, seq_start and workspace are required");
+  if (!compute_layout(d, L)) return fail(GDN_ERR_DIMS, "bad sizes");
+  if (a->workspace_bytes < L->pub.total) return fail(GDN_ERR_WORKSPACE, "workspace smaller than gdn_tree_workspace_size");
+  if (((uintptr_t)a->workspace & 255u) != 0) return fail(GDN_ERR_ARGS, "workspace must be 256-byte aligned");
+  if (a->n_out < 0 || a->n_state < 0) return fail(GDN_ERR_ARGS, "row counts must be >= 0");
+  if (a->n_state > 0 && !a->state_rows) return fail(GDN_ERR_NULL, "state_rows is NULL");
+  if (a->n_out > 0 && !a->out_rows && a->n_out != d.T) return fail(GDN_ERR_ARGS, "without out_rows, n_out must be T");
+  if (!walk) return GDN_OK;
+  if (!a->q || !a->k || !a->v || !a->log_gate || !a->beta) return fail(GDN_ERR_NULL, "q, k, v, log_gate and beta are required");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v)) return fail(GDN_ERR_ARGS, "q, k, v must be 16-byte aligned");
+  if (!a->out_rows && a->n_out != d.T) return fail(GDN_ERR_ARGS, "without out_rows, n_out must be T");
+  if ((a->n_out > 0 || (!a->out_rows && d.T > 0)) && !a->out) return fail(GDN_ERR_NULL, "out is NULL");
+  if (a->n_state > 0 && !a->state_out) return fail(GDN_ERR_NULL, "state_out is NULL");
+  if (a->dv_tile != 0) {
+    if (!walk_supported(d.dtype, d.Dk, a->dv_tile) || d.Dv % a->dv_tile)
+      return fail(GDN_ERR_ARGS, "dv_tile must be 0 or a supported width (16, 32, 64 bf16; 16, 32 fp32) dividing Dv");
+  }
+  const long long items = d.T * (long long)d.H * (d.Dv / 16);
+  if (items >= 0x7fffffffLL) return fail(GDN_ERR_DIMS, "T * H * Dv / 16 must stay below 2^31");
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_tree_version(void) { return GDN_TREE_VERSION; }
+
+const char* gdn_tree_last_error(void) { return g_last_error.c_str(); }
+
+const char* gdn_tree_strerror(int code) {
+  switch (code) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_DIMS: return "unsupported sizes";
+    case GDN_ERR_DTYPE: return "unknown dtype";
+    case GDN_ERR_WORKSPACE: return "workspace too small";
+    case GDN_ERR_HIP: return "HIP launch failed";
+    case GDN_ERR_ARGS: return "inconsistent arguments";
+    case 100 + GDN_DEV_OK: return "no device error";
+    case 100 + GDN_DEV_SEQ_START: return "seq_start is not a CSR over [0, T]";
+    case 100 + GDN_DEV_PARENT_ORDER: return "a parent is < -1 or not before its child";
+    case 100 + GDN_DEV_PARENT_SEQ: return "a parent lies in another sequence";
+    case 100 + GDN_DEV_FORK_CAPACITY: return "more fork tokens than max_forks";
+    case 100 + GDN_DEV_LEVEL_CAPACITY: return "fork nesting reaches max_levels";
+    case 100 + GDN_DEV_ROWS: return "an out/state row is out of range or repeated";
+    case 100 + GDN_DEV_PATH: return "a commit path is not a root-to-node parent chain";
+    default: return "unknown code";
+  }
+}
+
+int gdn_tree_workspace_size(const gdn_tree_dims* dims, size_t* bytes) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!bytes) return fail(GDN_ERR_NULL, "bytes is NULL");
+  LayoutFull L;
+  if (!compute_layout(*dims, &L)) return fail(GDN_ERR_DIMS, "bad sizes");
+  *bytes = L.pub.total;
+  return GDN_OK;
+}
+
+int gdn_tree_plan_layout(const gdn_tree_dims* dims, gdn_tree_layout* layout) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!layout) return fail(GDN_ERR_NULL, "layout is NULL");
+  LayoutFull L;
+  if (!compute_layout(*dims, &L)) return fail(GDN_ERR_DIMS, "bad sizes");
+  *layout = L.pub;
+  return GDN_OK;
+}
+
+size_t gdn_tree_commit_workspace_size(void) { return 256; }
+
+int gdn_tree_plan(const gdn_tree_fwd_args* a, void* stream) {
+  LayoutFull L;
+  int rc = check_fwd(a, false, &L);
+  if (rc) return rc;
+  Meta m = meta_from(a->workspace, L);
+  hipError_t e = launch_plan(*a, m, L, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "gdn_tree_plan");
+  return GDN_OK;
+}
+
+int gdn_tree_forward(const gdn_tree_fwd_args* a, void* stream) {
+  LayoutFull L;
+  int rc = check_fwd(a, true, &L);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  Meta m = meta_from(a->workspace, L);
+  hipError_t e = launch_plan(*a, m, L, s);
+  if (e != hipSuccess) return fail_hip(e, "gdn_tree_forward (metadata)");
+  if (a->dims.T == 0 || a->dims.n_seq == 0) return GDN_OK;
+  const int bv = a->dv_tile ? a->dv_tile : choose_dv_tile(a->dims);
+  e = launch_walk(*a, m, bv, s);
+  if (e != hipSuccess) return fail_hip(e, "gdn_tree_forward (walk)");
+  return GDN_OK;
+}
+
+int gdn_tree_commit(const gdn_tree_commit_args* a, void* stream) {
+  if (!a) return fail(GDN_ERR_NULL, "args is NULL");
+  gdn_tree_dims d = a->dims;
+  d.max_forks = 0;
+  d.max_levels = 1;
+  int rc = check_dims(&d);
+  if (rc) return rc;
+  if (a->n_path < 0) return fail(GDN_ERR_ARGS, "n_path must be >= 0");
+  if (!a->workspace) return fail(GDN_ERR_NULL, "workspace is NULL");
+  if (a->workspace_bytes < gdn_tree_commit_workspace_size()) return fail(GDN_ERR_WORKSPACE, "commit workspace too small");
+  if (a->n_path > 0) {
+    if (!a->k || !a->log_gate || !a->parent_idx || !a->seq_start || !a->pseudo_v || !a->path_ptr || !a->path_seq ||
+        !a->out_state)
+      return fail(GDN_ERR_NULL, "k, log_gate, parent_idx, seq_start, pseudo_v, path_ptr, path_seq and out_state are required");
+    if (!aligned16(a->out_state) || (a->init_state && !aligned16(a->init_state)))
+      return fail(GDN_ERR_ARGS, "states must be 16-byte aligned");
+  }
+  hipError_t e = launch_commit(*a, (unsigned long long*)a->workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "gdn_tree_commit");
+  return GDN_OK;
+}
+
+int gdn_tree_check_error(const void* workspace, void* stream, int32_t* code, int64_t* index) {
+  if (!workspace || !code || !index) return fail(GDN_ERR_NULL, "workspace, code and index are required");
+  unsigned long long word = 0;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return fail_hip(e, "gdn_tree_check_error (copy)");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail_hip(e, "gdn_tree_check_error (sync)");
+  if (word == kNoError) {
+    *code = GDN_DEV_OK;
+    *index = 0;
+  } else {
+    *code = (int32_t)(word >> 32);
+    *index = (int64_t)(uint32_t)(word & 0xffffffffu);
+  }
+  return GDN_OK;
+}
+
+}  // extern "C"

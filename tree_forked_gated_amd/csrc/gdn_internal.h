@@ -1,0 +1,71 @@
+// Internal declarations shared by the HIP sources of the gdn_tree library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_tree.h"
+
+namespace gdn {
+
+constexpr int kChunk = GDN_TREE_CHUNK;  // rows of one tree-WY chunk
+constexpr int kThreads = 256;           // workgroup of the walk: four wave64s
+constexpr unsigned long long kNoError = ~0ull;
+constexpr int kUnmapped = 0x7fffffff;  // out_map / state_map entry of a token nobody asked for
+
+// Error word: the smallest (code << 32 | index) any kernel raised.
+__device__ inline void raise_error(unsigned long long* err, int code, long long index) {
+  atomicMin(err, ((unsigned long long)(unsigned)code << 32) | (unsigned long long)(uint32_t)index);
+}
+
+// Device pointers into a forward workspace (see gdn_tree_layout for the public part).
+struct Meta {
+  unsigned long long* err;
+  int* n_seg;
+  int* n_fork;
+  int* tok_seq;
+  int* depth;
+  int* fork_slot;
+  int* seg_start;
+  int* seg_len;
+  int* seg_seq;
+  int* seg_mode;
+  int* seg_entry;
+  int* seg_slot;
+  int* seg_level;
+  int* level_count;
+  int* level_ptr;
+  int* level_items;
+  unsigned long long* tree_mask;
+  float* fork_states;
+  // internal tables
+  int* is_start;
+  int* is_fork;
+  int* out_map;
+  int* state_map;
+  int* seg_depth0;
+  int* level_fill;
+  int* walk_ctr;
+  int* scan_sums;  // [2 * n_scan_blocks] block totals, then their exclusive offsets
+};
+
+constexpr int kScanTile = 4096;  // tokens per block of the metadata scans
+
+struct LayoutFull {
+  gdn_tree_layout pub;
+  size_t is_start, is_fork, out_map, state_map, seg_depth0, level_fill, walk_ctr, scan_sums;
+  int n_scan_blocks;
+};
+
+// Host: byte offsets of every table for these sizes (256-byte aligned).
+bool compute_layout(const gdn_tree_dims& d, LayoutFull* L);
+Meta meta_from(void* workspace, const LayoutFull& L);
+
+// Host launchers (enqueue only). Return hipSuccess or the launch error.
+hipError_t launch_plan(const gdn_tree_fwd_args& a, const Meta& m, const LayoutFull& L, hipStream_t s);
+hipError_t launch_walk(const gdn_tree_fwd_args& a, const Meta& m, int bv, hipStream_t s);
+hipError_t launch_commit(const gdn_tree_commit_args& a, unsigned long long* err, hipStream_t s);
+bool walk_supported(int dtype, int dk, int bv);
+int walk_lds_bytes(int dtype, int dk, int bv);
+
+}  // namespace gdn

@@ -1,0 +1,419 @@
+// Tree metadata built on the GPU, before the walk reads it.
+//
+// Flide ("Accelerating Decision Inference with Exact State Forking", section
+// 3.3.1) keeps every quantity that depends on the round's composition in
+// compact device buffers that the kernels read, so launch shapes depend only
+// on the stream length. Here the launch grids depend only on T, n_seq and the
+// capacities; the tree itself is data.
+//
+// Rules (the chunking is this library's own; the pages fix only that a
+// question's chunks start exactly at its fork, Flide section 3.5, and that a
+// draft tree is solved as one triangular system, TreeWY "Speculative
+// Verification for Gated DeltaNet Hybrids" section 3, Eq. 2):
+//  * a sequence of at most 64 tokens is one tree chunk with a 64 x 64
+//    ancestor-or-self bit mask;
+//  * a longer sequence is cut into segments, each starting at a token whose
+//    parent is not the token just before it; each segment into 64-token chunks
+//    from its start;
+//  * the parent of a segment start is a fork token and owns a fork-state slot
+//    (slots numbered in stream order); the segment's level is the level of the
+//    segment holding its fork token plus one, 0 from an initial state.
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+__device__ inline int upper_bound_seq(const int* seq_start, int n_seq, int t) {
+  // largest s in [0, n_seq) with seq_start[s] <= t (seq_start validated separately; never reads out of range)
+  int lo = 0, hi = n_seq;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (seq_start[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ inline int seg_of(const int* seg_start, int n_seg, int t) {
+  int lo = 0, hi = n_seg;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (seg_start[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// True when seq_start failed validation: later kernels must not index with it.
+__device__ inline bool bad_csr(const Meta& m) { return (*m.err >> 32) == (unsigned long long)GDN_DEV_SEQ_START; }
+
+__global__ void k_init(Meta m, int T, int n_seq, int max_levels) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < T) {
+    m.out_map[i] = kUnmapped;
+    m.state_map[i] = kUnmapped;
+    m.is_fork[i] = 0;
+    m.is_start[i] = 0;
+    m.fork_slot[i] = -1;
+    m.depth[i] = 0;
+  }
+  if (i < (long long)n_seq * kChunk) m.tree_mask[i] = 0ull;
+  if (i < max_levels) {
+    m.level_count[i] = 0;
+    m.level_fill[i] = 0;
+    m.walk_ctr[i] = 0;
+  }
+  if (i == 0) {
+    *m.err = kNoError;
+    *m.n_seg = 0;
+    *m.n_fork = 0;
+  }
+}
+
+__global__ void k_seq_check(const int* seq_start, int n_seq, int T, Meta m) {
+  int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s > n_seq) return;
+  int v = seq_start[s];
+  if (s == 0) {
+    if (v != 0) raise_error(m.err, GDN_DEV_SEQ_START, 0);
+    return;
+  }
+  if (v < seq_start[s - 1] || v > T) raise_error(m.err, GDN_DEV_SEQ_START, s);
+  else if (s == n_seq && v != T) raise_error(m.err, GDN_DEV_SEQ_START, s);
+}
+
+__global__ void k_tokens(const int* parent, const int* seq_start, int n_seq, int T, Meta m) {
+  int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T || bad_csr(m)) return;
+  int s = upper_bound_seq(seq_start, n_seq, t);
+  m.tok_seq[t] = s;
+  int a = seq_start[s], b = seq_start[s + 1];
+  bool tree = (b - a) <= kChunk;
+  int p = parent[t];
+  bool ok = true;
+  if (p < -1 || p >= t) {
+    raise_error(m.err, GDN_DEV_PARENT_ORDER, t);
+    ok = false;
+  } else if (p >= 0 && p < a) {
+    raise_error(m.err, GDN_DEV_PARENT_SEQ, t);
+    ok = false;
+  }
+  int start = tree ? (t == a) : (p < 0 || p != t - 1);
+  m.is_start[t] = start;
+  if (!tree && start && ok && p >= 0) m.is_fork[p] = 1;
+}
+
+__global__ void k_rows(const int* rows, int n, int T, int* map, unsigned long long* err) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  int r = rows[i];
+  if (r < 0 || r >= T) raise_error(err, GDN_DEV_ROWS, i);
+  else atomicMin(&map[r], i);
+}
+
+__global__ void k_rows_check(const int* rows, int n, int T, const int* map, unsigned long long* err) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  int r = rows[i];
+  if (r >= 0 && r < T && map[r] != i) raise_error(err, GDN_DEV_ROWS, i);
+}
+
+// ---- exclusive scans of is_start (segment ids) and is_fork (slot ids)
+
+__device__ inline int block_excl_scan(int v, int* sh, int* total) {
+  // 256-thread exclusive scan through LDS (Hillis-Steele on the inclusive form)
+  int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    int x = (tid >= off) ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += x;
+    __syncthreads();
+  }
+  int incl = sh[tid];
+  *total = sh[255];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ void __launch_bounds__(256) k_scan_reduce(int T, Meta m) {
+  __shared__ int sh[256];
+  int base = blockIdx.x * kScanTile;
+  int a = 0, f = 0;
+  for (int i = threadIdx.x; i < kScanTile; i += 256) {
+    int t = base + i;
+    if (t < T) { a += m.is_start[t]; f += m.is_fork[t]; }
+  }
+  int ta, tf;
+  block_excl_scan(a, sh, &ta);
+  block_excl_scan(f, sh, &tf);
+  if (threadIdx.x == 0) {
+    m.scan_sums[2 * blockIdx.x] = ta;
+    m.scan_sums[2 * blockIdx.x + 1] = tf;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_scan_top(int nb, Meta m) {
+  __shared__ int sh[256];
+  int* offs = m.scan_sums + 2 * nb;
+  int run_a = 0, run_f = 0;
+  for (int c = 0; c < nb; c += 256) {
+    int i = c + threadIdx.x;
+    int a = (i < nb) ? m.scan_sums[2 * i] : 0;
+    int f = (i < nb) ? m.scan_sums[2 * i + 1] : 0;
+    int ta, tf;
+    int ea = block_excl_scan(a, sh, &ta);
+    int ef = block_excl_scan(f, sh, &tf);
+    if (i < nb) {
+      offs[2 * i] = run_a + ea;
+      offs[2 * i + 1] = run_f + ef;
+    }
+    run_a += ta;
+    run_f += tf;
+  }
+  if (threadIdx.x == 0) {
+    *m.n_seg = run_a;
+    *m.n_fork = run_f;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_scan_apply(int T, int nb, int max_forks, Meta m) {
+  __shared__ int sh[256];
+  constexpr int per = kScanTile / 256;
+  int base = blockIdx.x * kScanTile + threadIdx.x * per;
+  int a = 0, f = 0;
+  for (int i = 0; i < per; ++i) {
+    int t = base + i;
+    if (t < T) { a += m.is_start[t]; f += m.is_fork[t]; }
+  }
+  int ta, tf;
+  int ea = block_excl_scan(a, sh, &ta) + m.scan_sums[2 * nb + 2 * blockIdx.x];
+  int ef = block_excl_scan(f, sh, &tf) + m.scan_sums[2 * nb + 2 * blockIdx.x + 1];
+  for (int i = 0; i < per; ++i) {
+    int t = base + i;
+    if (t >= T) break;
+    if (m.is_start[t]) m.seg_start[ea++] = t;
+    if (m.is_fork[t]) {
+      if (ef == max_forks) raise_error(m.err, GDN_DEV_FORK_CAPACITY, t);
+      m.fork_slot[t] = ef++;
+    }
+  }
+}
+
+__global__ void k_segments(const int* parent, const int* seq_start, int T, Meta m) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  int n_seg = *m.n_seg;
+  if (i >= n_seg || bad_csr(m)) return;
+  int start = m.seg_start[i];
+  int end = (i + 1 < n_seg) ? m.seg_start[i + 1] : T;
+  int s = m.tok_seq[start];
+  int mode = (seq_start[s + 1] - seq_start[s]) <= kChunk ? 1 : 0;
+  int e = mode ? -1 : parent[start];
+  if (e < 0 || e >= start) e = -1;  // invalid parents were reported; never follow them
+  m.seg_len[i] = end - start;
+  m.seg_seq[i] = s;
+  m.seg_mode[i] = mode;
+  m.seg_entry[i] = e;
+  m.seg_slot[i] = (e >= 0) ? m.fork_slot[e] : -1;
+}
+
+__global__ void k_levels(int max_levels, Meta m) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  int n_seg = *m.n_seg;
+  if (i >= n_seg) return;
+  int lv = 0, d = 0, cur = i;
+  for (;;) {
+    int e = m.seg_entry[cur];
+    if (e < 0) break;
+    if (lv + 1 >= max_levels) {
+      raise_error(m.err, GDN_DEV_LEVEL_CAPACITY, m.seg_start[i]);
+      lv = max_levels;
+      break;
+    }
+    ++lv;
+    int j = seg_of(m.seg_start, n_seg, e);
+    d += e - m.seg_start[j] + 1;
+    cur = j;
+  }
+  m.seg_level[i] = lv;
+  m.seg_depth0[i] = d;
+  if (lv < max_levels) atomicAdd(&m.level_count[lv], 1);
+}
+
+__global__ void k_level_ptr(int max_levels, Meta m) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int run = 0;
+  for (int l = 0; l < max_levels; ++l) {
+    m.level_ptr[l] = run;
+    run += m.level_count[l];
+  }
+  m.level_ptr[max_levels] = run;
+}
+
+__global__ void k_level_fill(int max_levels, Meta m) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= *m.n_seg) return;
+  int lv = m.seg_level[i];
+  if (lv >= max_levels) return;
+  int pos = atomicAdd(&m.level_fill[lv], 1);
+  m.level_items[m.level_ptr[lv] + pos] = i;
+}
+
+__global__ void k_depth(const int* seq_start, int T, Meta m) {
+  int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T || bad_csr(m)) return;
+  int s = m.tok_seq[t];
+  if (seq_start[s + 1] - seq_start[s] <= kChunk) return;  // tree chunks: k_tree_meta
+  int j = seg_of(m.seg_start, *m.n_seg, t);
+  m.depth[t] = m.seg_depth0[j] + (t - m.seg_start[j]);
+}
+
+// One wave per sequence: depth and ancestor-or-self masks of a tree chunk by
+// pointer jumping (six rounds cover 64 levels).
+__global__ void __launch_bounds__(64) k_tree_meta(const int* parent, const int* seq_start, Meta m) {
+  int s = blockIdx.x;
+  if (bad_csr(m)) return;
+  int a = seq_start[s], n = seq_start[s + 1] - a;
+  if (n <= 0 || n > kChunk) return;
+  int i = threadIdx.x;
+  int p = -1;
+  if (i < n) {
+    int g = parent[a + i];
+    p = (g >= a && g < a + i) ? g - a : -1;
+  }
+  unsigned long long anc = (i < n) ? (1ull << i) : 0ull;
+  int d = (p >= 0) ? 1 : 0;
+  for (int r = 0; r < 6; ++r) {
+    int src = p >= 0 ? p : i;
+    unsigned long long panc = __shfl(anc, src);
+    int pd = __shfl(d, src);
+    int pp = __shfl(p, src);
+    if (p >= 0) {
+      anc |= panc;
+      d += pd;
+      p = pp;
+    }
+  }
+  if (i < n) {
+    m.tree_mask[(size_t)s * kChunk + i] = anc;
+    m.depth[a + i] = d;
+  }
+}
+
+inline int blocks_for(long long n, int bs) { return (int)((n + bs - 1) / bs); }
+
+}  // namespace
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool compute_layout(const gdn_tree_dims& d, LayoutFull* L) {
+  if (d.T < 0 || d.T > 0x7fffffff || d.n_seq < 0 || d.max_forks < 0 || d.max_levels < 1) return false;
+  size_t T = (size_t)d.T;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  gdn_tree_layout& p = L->pub;
+  p.err = take(8);
+  p.n_seg = take(4);
+  p.n_fork = take(4);
+  p.tok_seq = take(4 * T);
+  p.depth = take(4 * T);
+  p.fork_slot = take(4 * T);
+  p.seg_start = take(4 * T);
+  p.seg_len = take(4 * T);
+  p.seg_seq = take(4 * T);
+  p.seg_mode = take(4 * T);
+  p.seg_entry = take(4 * T);
+  p.seg_slot = take(4 * T);
+  p.seg_level = take(4 * T);
+  p.level_count = take(4 * (size_t)d.max_levels);
+  p.level_ptr = take(4 * ((size_t)d.max_levels + 1));
+  p.level_items = take(4 * T);
+  p.tree_mask = take(8 * (size_t)d.n_seq * kChunk);
+  L->is_start = take(4 * T);
+  L->is_fork = take(4 * T);
+  L->out_map = take(4 * T);
+  L->state_map = take(4 * T);
+  L->seg_depth0 = take(4 * T);
+  L->level_fill = take(4 * (size_t)d.max_levels);
+  L->walk_ctr = take(4 * (size_t)d.max_levels);
+  L->n_scan_blocks = (int)((T + kScanTile - 1) / kScanTile);
+  if (L->n_scan_blocks < 1) L->n_scan_blocks = 1;
+  L->scan_sums = take(4 * 4 * (size_t)L->n_scan_blocks);
+  size_t state_elems = (size_t)d.H * d.Dv * d.Dk;
+  p.fork_states = take(4 * state_elems * (size_t)d.max_forks);
+  p.total = off;
+  return true;
+}
+
+Meta meta_from(void* ws, const LayoutFull& L) {
+  char* b = (char*)ws;
+  const gdn_tree_layout& p = L.pub;
+  Meta m;
+  m.err = (unsigned long long*)(b + p.err);
+  m.n_seg = (int*)(b + p.n_seg);
+  m.n_fork = (int*)(b + p.n_fork);
+  m.tok_seq = (int*)(b + p.tok_seq);
+  m.depth = (int*)(b + p.depth);
+  m.fork_slot = (int*)(b + p.fork_slot);
+  m.seg_start = (int*)(b + p.seg_start);
+  m.seg_len = (int*)(b + p.seg_len);
+  m.seg_seq = (int*)(b + p.seg_seq);
+  m.seg_mode = (int*)(b + p.seg_mode);
+  m.seg_entry = (int*)(b + p.seg_entry);
+  m.seg_slot = (int*)(b + p.seg_slot);
+  m.seg_level = (int*)(b + p.seg_level);
+  m.level_count = (int*)(b + p.level_count);
+  m.level_ptr = (int*)(b + p.level_ptr);
+  m.level_items = (int*)(b + p.level_items);
+  m.tree_mask = (unsigned long long*)(b + p.tree_mask);
+  m.fork_states = (float*)(b + p.fork_states);
+  m.is_start = (int*)(b + L.is_start);
+  m.is_fork = (int*)(b + L.is_fork);
+  m.out_map = (int*)(b + L.out_map);
+  m.state_map = (int*)(b + L.state_map);
+  m.seg_depth0 = (int*)(b + L.seg_depth0);
+  m.level_fill = (int*)(b + L.level_fill);
+  m.walk_ctr = (int*)(b + L.walk_ctr);
+  m.scan_sums = (int*)(b + L.scan_sums);
+  return m;
+}
+
+hipError_t launch_plan(const gdn_tree_fwd_args& a, const Meta& m, const LayoutFull& L, hipStream_t s) {
+  const int T = (int)a.dims.T, n_seq = a.dims.n_seq, ml = a.dims.max_levels;
+  const int bs = 256;
+  long long init_n = T;
+  if ((long long)n_seq * kChunk > init_n) init_n = (long long)n_seq * kChunk;
+  if (ml > init_n) init_n = ml;
+  if (init_n < 1) init_n = 1;
+  const int gT = blocks_for(T > 0 ? T : 1, bs);
+  hipLaunchKernelGGL(k_init, dim3(blocks_for(init_n, bs)), dim3(bs), 0, s, m, T, n_seq, ml);
+  hipLaunchKernelGGL(k_seq_check, dim3(blocks_for(n_seq + 1, bs)), dim3(bs), 0, s, a.seq_start, n_seq, T, m);
+  if (T > 0 && n_seq > 0)
+    hipLaunchKernelGGL(k_tokens, dim3(gT), dim3(bs), 0, s, a.parent_idx, a.seq_start, n_seq, T, m);
+  if (a.out_rows && a.n_out > 0) {
+    hipLaunchKernelGGL(k_rows, dim3(blocks_for(a.n_out, bs)), dim3(bs), 0, s, a.out_rows, a.n_out, T, m.out_map, m.err);
+    hipLaunchKernelGGL(k_rows_check, dim3(blocks_for(a.n_out, bs)), dim3(bs), 0, s, a.out_rows, a.n_out, T, m.out_map,
+                       m.err);
+  }
+  if (a.state_rows && a.n_state > 0) {
+    hipLaunchKernelGGL(k_rows, dim3(blocks_for(a.n_state, bs)), dim3(bs), 0, s, a.state_rows, a.n_state, T,
+                       m.state_map, m.err);
+    hipLaunchKernelGGL(k_rows_check, dim3(blocks_for(a.n_state, bs)), dim3(bs), 0, s, a.state_rows, a.n_state, T,
+                       m.state_map, m.err);
+  }
+  if (T > 0 && n_seq > 0) {
+    const int nb = L.n_scan_blocks;
+    hipLaunchKernelGGL(k_scan_reduce, dim3(nb), dim3(256), 0, s, T, m);
+    hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(256), 0, s, nb, m);
+    hipLaunchKernelGGL(k_scan_apply, dim3(nb), dim3(256), 0, s, T, nb, a.dims.max_forks, m);
+    hipLaunchKernelGGL(k_segments, dim3(gT), dim3(bs), 0, s, a.parent_idx, a.seq_start, T, m);
+    hipLaunchKernelGGL(k_levels, dim3(gT), dim3(bs), 0, s, ml, m);
+    hipLaunchKernelGGL(k_level_ptr, dim3(1), dim3(64), 0, s, ml, m);
+    hipLaunchKernelGGL(k_level_fill, dim3(gT), dim3(bs), 0, s, ml, m);
+    hipLaunchKernelGGL(k_depth, dim3(gT), dim3(bs), 0, s, a.seq_start, T, m);
+    hipLaunchKernelGGL(k_tree_meta, dim3(n_seq), dim3(64), 0, s, a.parent_idx, a.seq_start, m);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdn
