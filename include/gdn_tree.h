@@ -59,6 +59,21 @@ typedef enum gdn_dtype {
   GDN_BF16 = 1, /* q, k, v, log_gate, beta and out in bf16 (states stay fp32) */
 } gdn_dtype;
 
+/* Forward flags.
+ * GDN_FWD_PLANNED: the workspace already holds the metadata that
+ *   gdn_tree_plan (or an earlier gdn_tree_forward) built from the same dims,
+ *   parent_idx, seq_start, out_rows and state_rows, and nothing has written
+ *   the workspace since; the metadata kernels are skipped and only the walk
+ *   runs. The tree is the same for every GDN layer of a round (Flide,
+ *   "Accelerating Decision Inference with Exact State Forking", section 3.3.1:
+ *   metadata is filled once before the round's graph replays), so a model
+ *   plans once and walks once per layer. The plan stamps the workspace with
+ *   a fingerprint of dims, n_out, n_state and whether out_rows is given; a
+ *   walk whose fingerprint differs raises GDN_DEV_NOT_PLANNED and computes
+ *   nothing. A workspace planned for another tree of the same sizes gives
+ *   that tree's results (never a fault: every table stays within its sizes). */
+#define GDN_FWD_PLANNED 1u
+
 typedef enum gdn_status {
   GDN_OK = 0,
   GDN_ERR_NULL = -1,      /* a required pointer is NULL */
@@ -79,6 +94,7 @@ typedef enum gdn_dev_error {
   GDN_DEV_LEVEL_CAPACITY = 5, /* fork nesting reaches max_levels; index = first token of the segment */
   GDN_DEV_ROWS = 6,           /* out_rows / state_rows entry outside [0, T) or repeated; index = position */
   GDN_DEV_PATH = 7,           /* commit path is not a root-to-node parent chain; index = path number */
+  GDN_DEV_NOT_PLANNED = 8,    /* GDN_FWD_PLANNED on a workspace without a matching plan; index = 0 */
 } gdn_dev_error;
 
 /*
@@ -124,7 +140,7 @@ typedef struct gdn_tree_dims {
  *                            error word; contents need no initialisation
  *  dv_tile                   columns of Dv one workgroup carries: 0 = automatic, else 16, 32
  *                            or 64 dividing Dv. Results are bitwise the same for every choice.
- *  flags                     reserved, 0
+ *  flags                     0 or GDN_FWD_PLANNED
  */
 typedef struct gdn_tree_fwd_args {
   gdn_tree_dims dims;

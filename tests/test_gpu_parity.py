@@ -86,3 +86,33 @@ def test_dv_tiles_bitwise_identical(dv_tile):
     assert np.array_equal(res.out.view(dtype=base.out.dtype).cpu().float().numpy(), base.out.cpu().float().numpy())
     assert np.array_equal(res.state.cpu().numpy(), base.state.cpu().numpy())
     assert np.array_equal(res.pseudo_v.cpu().numpy(), base.pseudo_v.cpu().numpy())
+
+
+def test_planned_walk_is_bitwise_the_full_forward():
+    """GDN_FWD_PLANNED reuses the workspace's metadata: the walk alone gives the
+    same bits as a forward that plans first; a workspace planned for other
+    sizes is refused on the device (GDN_DEV_NOT_PLANNED) instead of walked."""
+    import torch
+    from tree_forked_gated_amd import binding as B
+    wl = W.random_small(31, n_seq=4, H=2, Dk=64, Dv=64, dtype="bf16", max_len=300)
+    rows = W.leaves_of(wl.parent)
+    say("planned walk vs full forward")
+    base, d = run_forward(wl, keep_pseudo=True, state_rows=rows)
+    ws = base.workspace
+    out2 = torch.empty_like(base.out)
+    st2 = torch.empty_like(base.state)
+    pv2 = torch.empty_like(base.pseudo_v)
+    cap = B.capacities(wl.parent, wl.seq_start)
+    B.forward(d["q"], d["k"], d["v"], d["log_gate"], d["beta"], d["parent_idx"], d["seq_start"], d["init_state"],
+              state_rows=rows, keep_pseudo=True, workspace=ws, out=out2, state_out=st2, pseudo_v=pv2,
+              max_forks=cap["max_forks"], max_levels=cap["max_levels"], planned=True, check=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, base.out) and torch.equal(st2, base.state) and torch.equal(pv2, base.pseudo_v)
+    # fewer state rows than the plan was built for: refused, nothing written
+    st3 = torch.full_like(base.state[:1], 7.0)
+    B.forward(d["q"], d["k"], d["v"], d["log_gate"], d["beta"], d["parent_idx"], d["seq_start"], d["init_state"],
+              state_rows=rows[:1], keep_pseudo=False, workspace=ws, state_out=st3,
+              max_forks=cap["max_forks"], max_levels=cap["max_levels"], planned=True)
+    code, _ = B.check_error(ws)
+    assert code == 8
+    assert bool((st3 == 7.0).all())

@@ -20,8 +20,9 @@ LIB_PATH = os.path.join(_HERE, "libgdn_tree.so")
 
 GDN_F32, GDN_BF16 = 0, 1
 DEV_ERRORS = {0: "ok", 1: "seq_start", 2: "parent order", 3: "parent in another sequence", 4: "fork capacity",
-              5: "level capacity", 6: "rows", 7: "commit path"}
+              5: "level capacity", 6: "rows", 7: "commit path", 8: "workspace not planned for these sizes"}
 CHUNK = 64
+FWD_PLANNED = 1  # gdn_tree.h GDN_FWD_PLANNED: reuse the metadata already in the workspace
 
 
 class Dims(ctypes.Structure):
@@ -188,7 +189,7 @@ class ForwardResult:
 
 
 def _fwd_args(q, k, v, log_gate, beta, parent_idx, seq_start, init_state, out, out_rows, state_out, state_rows,
-              pseudo_v, workspace, dims, dv_tile):
+              pseudo_v, workspace, dims, dv_tile, flags=0):
     a = FwdArgs()
     a.dims = dims
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
@@ -205,7 +206,7 @@ def _fwd_args(q, k, v, log_gate, beta, parent_idx, seq_start, init_state, out, o
     a.workspace = _ptr(workspace)
     a.workspace_bytes = int(workspace.numel())
     a.dv_tile = int(dv_tile)
-    a.flags = 0
+    a.flags = int(flags)
     return a
 
 
@@ -219,7 +220,7 @@ def _i32(x, device):
 
 def forward(q, k, v, log_gate, beta, parent_idx, seq_start, init_state=None, *, out_rows=None, state_rows=None,
             keep_pseudo=False, max_forks=None, max_levels=None, dv_tile=0, workspace=None, out=None, state_out=None,
-            pseudo_v=None, stream=None, check=False) -> ForwardResult:
+            pseudo_v=None, stream=None, check=False, planned=False) -> ForwardResult:
     """gdn_tree_forward on torch tensors (device, contiguous).
 
     q, k [T,H,Dk], v [T,H,Dv], log_gate, beta [T,H] in float32 or bfloat16;
@@ -227,7 +228,9 @@ def forward(q, k, v, log_gate, beta, parent_idx, seq_start, init_state=None, *, 
     float32 or None. Returns out rows (all tokens unless out_rows), states of
     state_rows, pseudo-values when keep_pseudo, and the workspace (metadata and
     error word). max_forks / max_levels default to the tree's exact counts,
-    computed on the host (a synchronising convenience)."""
+    computed on the host (a synchronising convenience). planned=True reuses
+    the metadata that an earlier call built in ``workspace`` for the same
+    structure (GDN_FWD_PLANNED): only the walk runs."""
     device = q.device
     T, H, Dk = q.shape
     Dv = v.shape[2]
@@ -252,7 +255,7 @@ def forward(q, k, v, log_gate, beta, parent_idx, seq_start, init_state=None, *, 
     if keep_pseudo and pseudo_v is None:
         pseudo_v = torch.empty((T, H, Dv), dtype=torch.float32, device=device)
     a = _fwd_args(q, k, v, log_gate, beta, parent_idx, seq_start, init_state, out, out_rows, state_out, state_rows,
-                  pseudo_v, workspace, dims, dv_tile)
+                  pseudo_v, workspace, dims, dv_tile, FWD_PLANNED if planned else 0)
     _check(lib.gdn_tree_forward(ctypes.byref(a), _stream(stream)), "gdn_tree_forward")
     if check:
         raise_device_error(workspace, stream)

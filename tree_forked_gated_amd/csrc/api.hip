@@ -67,6 +67,7 @@ int check_fwd(const gdn_tree_fwd_args* a, bool walk, LayoutFull* L) {
   if (a->n_out < 0 || a->n_state < 0) return fail(GDN_ERR_ARGS, "row counts must be >= 0");
   if (a->n_state > 0 && !a->state_rows) return fail(GDN_ERR_NULL, "state_rows is NULL");
   if (a->n_out > 0 && !a->out_rows && a->n_out != d.T) return fail(GDN_ERR_ARGS, "without out_rows, n_out must be T");
+  if (a->flags & ~GDN_FWD_PLANNED) return fail(GDN_ERR_ARGS, "unknown flags");
   if (!walk) return GDN_OK;
   if (!a->q || !a->k || !a->v || !a->log_gate || !a->beta) return fail(GDN_ERR_NULL, "q, k, v, log_gate and beta are required");
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v)) return fail(GDN_ERR_ARGS, "q, k, v must be 16-byte aligned");
@@ -107,6 +108,7 @@ const char* gdn_tree_strerror(int code) {
     case 100 + GDN_DEV_LEVEL_CAPACITY: return "fork nesting reaches max_levels";
     case 100 + GDN_DEV_ROWS: return "an out/state row is out of range or repeated";
     case 100 + GDN_DEV_PATH: return "a commit path is not a root-to-node parent chain";
+    case 100 + GDN_DEV_NOT_PLANNED: return "GDN_FWD_PLANNED on a workspace without a matching plan";
     default: return "unknown code";
   }
 }
@@ -138,7 +140,7 @@ int gdn_tree_plan(const gdn_tree_fwd_args* a, void* stream) {
   int rc = check_fwd(a, false, &L);
   if (rc) return rc;
   Meta m = meta_from(a->workspace, L);
-  hipError_t e = launch_plan(*a, m, L, (hipStream_t)stream);
+  hipError_t e = launch_plan(*a, m, L, plan_fingerprint(*a), (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "gdn_tree_plan");
   return GDN_OK;
 }
@@ -149,7 +151,9 @@ int gdn_tree_forward(const gdn_tree_fwd_args* a, void* stream) {
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   Meta m = meta_from(a->workspace, L);
-  hipError_t e = launch_plan(*a, m, L, s);
+  const unsigned long long tag = plan_fingerprint(*a);
+  hipError_t e = (a->flags & GDN_FWD_PLANNED) ? launch_replan_check(m, a->dims.max_levels, tag, s)
+                                               : launch_plan(*a, m, L, tag, s);
   if (e != hipSuccess) return fail_hip(e, "gdn_tree_forward (metadata)");
   if (a->dims.T == 0 || a->dims.n_seq == 0) return GDN_OK;
   const int bv = a->dv_tile ? a->dv_tile : choose_dv_tile(a->dims);

@@ -47,13 +47,16 @@ struct Meta {
   int* level_fill;
   int* walk_ctr;
   int* scan_sums;  // [2 * n_scan_blocks] block totals, then their exclusive offsets
+  unsigned long long* plan_tag;  // fingerprint of the sizes the metadata was built for
+  int4* unit_info;  // per level entry (level_items order): {start, len, mode | seq << 1, fork slot}
 };
 
 constexpr int kScanTile = 4096;  // tokens per block of the metadata scans
+constexpr int kWalkQueues = 8;  // work counters per level: one per XCD of the walk's grid
 
 struct LayoutFull {
   gdn_tree_layout pub;
-  size_t is_start, is_fork, out_map, state_map, seg_depth0, level_fill, walk_ctr, scan_sums;
+  size_t is_start, is_fork, out_map, state_map, seg_depth0, level_fill, walk_ctr, scan_sums, plan_tag, unit_info;
   int n_scan_blocks;
 };
 
@@ -62,10 +65,20 @@ bool compute_layout(const gdn_tree_dims& d, LayoutFull* L);
 Meta meta_from(void* workspace, const LayoutFull& L);
 
 // Host launchers (enqueue only). Return hipSuccess or the launch error.
-hipError_t launch_plan(const gdn_tree_fwd_args& a, const Meta& m, const LayoutFull& L, hipStream_t s);
+hipError_t launch_plan(const gdn_tree_fwd_args& a, const Meta& m, const LayoutFull& L, unsigned long long tag,
+                       hipStream_t s);
+// Before a walk over an already planned workspace: checks the fingerprint and
+// clears the walk's work counters.
+hipError_t launch_replan_check(const Meta& m, int max_levels, unsigned long long tag, hipStream_t s);
+// Fingerprint of the sizes a plan depends on (never 0).
+unsigned long long plan_fingerprint(const gdn_tree_fwd_args& a);
 hipError_t launch_walk(const gdn_tree_fwd_args& a, const Meta& m, int bv, hipStream_t s);
 hipError_t launch_commit(const gdn_tree_commit_args& a, unsigned long long* err, hipStream_t s);
 bool walk_supported(int dtype, int dk, int bv);
+// MFMA walk for bf16 inputs with d_k = 128 (d_v tiles of 16, 32 or 64 columns)
+bool walk_mfma_supported(int dtype, int dk, int bv);
+bool walk_mfma_fits(const gdn_tree_dims& d);  // sizes within its 32-bit offsets
+hipError_t launch_walk_mfma(const gdn_tree_fwd_args& a, const Meta& m, int bv, hipStream_t s);
 int walk_lds_bytes(int dtype, int dk, int bv);
 
 }  // namespace gdn

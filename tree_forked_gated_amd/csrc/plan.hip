@@ -60,13 +60,24 @@ __global__ void k_init(Meta m, int T, int n_seq, int max_levels) {
   if (i < max_levels) {
     m.level_count[i] = 0;
     m.level_fill[i] = 0;
-    m.walk_ctr[i] = 0;
   }
+  if (i < (long long)max_levels * kWalkQueues) m.walk_ctr[i] = 0;
   if (i == 0) {
     *m.err = kNoError;
     *m.n_seg = 0;
     *m.n_fork = 0;
+    *m.plan_tag = 0ull;
   }
+}
+
+// Last kernel of a plan: the metadata is complete for these sizes.
+__global__ void k_plan_done(Meta m, unsigned long long tag) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *m.plan_tag = tag;
+}
+
+__global__ void k_replan_check(Meta m, int max_levels, unsigned long long tag) {
+  for (int i = threadIdx.x; i < max_levels * kWalkQueues; i += blockDim.x) m.walk_ctr[i] = 0;
+  if (threadIdx.x == 0 && *m.plan_tag != tag) raise_error(m.err, GDN_DEV_NOT_PLANNED, 0);
 }
 
 __global__ void k_seq_check(const int* seq_start, int n_seq, int T, Meta m) {
@@ -257,6 +268,8 @@ __global__ void k_level_fill(int max_levels, Meta m) {
   if (lv >= max_levels) return;
   int pos = atomicAdd(&m.level_fill[lv], 1);
   m.level_items[m.level_ptr[lv] + pos] = i;
+  m.unit_info[m.level_ptr[lv] + pos] = make_int4(m.seg_start[i], m.seg_len[i], m.seg_mode[i] | (m.seg_seq[i] << 1),
+                                                 m.seg_slot[i]);
 }
 
 __global__ void k_depth(const int* seq_start, int T, Meta m) {
@@ -335,10 +348,12 @@ bool compute_layout(const gdn_tree_dims& d, LayoutFull* L) {
   L->state_map = take(4 * T);
   L->seg_depth0 = take(4 * T);
   L->level_fill = take(4 * (size_t)d.max_levels);
-  L->walk_ctr = take(4 * (size_t)d.max_levels);
+  L->walk_ctr = take(4 * (size_t)d.max_levels * kWalkQueues);
   L->n_scan_blocks = (int)((T + kScanTile - 1) / kScanTile);
   if (L->n_scan_blocks < 1) L->n_scan_blocks = 1;
   L->scan_sums = take(4 * 4 * (size_t)L->n_scan_blocks);
+  L->plan_tag = take(8);
+  L->unit_info = take(16 * T);
   size_t state_elems = (size_t)d.H * d.Dv * d.Dk;
   p.fork_states = take(4 * state_elems * (size_t)d.max_forks);
   p.total = off;
@@ -375,15 +390,37 @@ Meta meta_from(void* ws, const LayoutFull& L) {
   m.level_fill = (int*)(b + L.level_fill);
   m.walk_ctr = (int*)(b + L.walk_ctr);
   m.scan_sums = (int*)(b + L.scan_sums);
+  m.plan_tag = (unsigned long long*)(b + L.plan_tag);
+  m.unit_info = (int4*)(b + L.unit_info);
   return m;
 }
 
-hipError_t launch_plan(const gdn_tree_fwd_args& a, const Meta& m, const LayoutFull& L, hipStream_t s) {
+unsigned long long plan_fingerprint(const gdn_tree_fwd_args& a) {
+  // FNV-1a over the sizes the tables depend on
+  const long long f[] = {a.dims.T, a.dims.H, a.dims.Dk, a.dims.Dv, a.dims.n_seq, a.dims.dtype, a.dims.max_forks,
+                         a.dims.max_levels, a.n_out, a.n_state, a.out_rows != nullptr, a.state_rows != nullptr};
+  unsigned long long h = 1469598103934665603ull;
+  for (long long x : f) {
+    for (int b = 0; b < 8; ++b) {
+      h ^= (unsigned long long)((x >> (8 * b)) & 0xff);
+      h *= 1099511628211ull;
+    }
+  }
+  return h ? h : 1ull;
+}
+
+hipError_t launch_replan_check(const Meta& m, int max_levels, unsigned long long tag, hipStream_t s) {
+  hipLaunchKernelGGL(k_replan_check, dim3(1), dim3(256), 0, s, m, max_levels, tag);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const gdn_tree_fwd_args& a, const Meta& m, const LayoutFull& L, unsigned long long tag,
+                       hipStream_t s) {
   const int T = (int)a.dims.T, n_seq = a.dims.n_seq, ml = a.dims.max_levels;
   const int bs = 256;
   long long init_n = T;
   if ((long long)n_seq * kChunk > init_n) init_n = (long long)n_seq * kChunk;
-  if (ml > init_n) init_n = ml;
+  if ((long long)ml * kWalkQueues > init_n) init_n = (long long)ml * kWalkQueues;
   if (init_n < 1) init_n = 1;
   const int gT = blocks_for(T > 0 ? T : 1, bs);
   hipLaunchKernelGGL(k_init, dim3(blocks_for(init_n, bs)), dim3(bs), 0, s, m, T, n_seq, ml);
@@ -413,6 +450,7 @@ hipError_t launch_plan(const gdn_tree_fwd_args& a, const Meta& m, const LayoutFu
     hipLaunchKernelGGL(k_depth, dim3(gT), dim3(bs), 0, s, a.seq_start, T, m);
     hipLaunchKernelGGL(k_tree_meta, dim3(n_seq), dim3(64), 0, s, a.parent_idx, a.seq_start, m);
   }
+  hipLaunchKernelGGL(k_plan_done, dim3(1), dim3(64), 0, s, m, tag);
   return hipGetLastError();
 }
 
