@@ -1,0 +1,315 @@
+"""Throughput of the tree-structured gated delta rule on one MI355X.
+
+One step = one gdn_tree_forward over one batch of synthetic input: the tree
+metadata built on the GPU, then the chunked tree-WY walk with its fork, leaf
+and output writes (plus, on the draft-tree workload, one gdn_tree_commit per
+accepted path). Inputs are resident in HBM before the timed region; several
+independent input sets rotate between steps so that the 256 MB last-level
+cache cannot hold the next step's operands.
+
+Prints one JSON line (last line of stdout). Progress goes to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--config {1,2,3,4}] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "tree-GDN tokens/s on 1 MI355X; fraction of bf16 MFMA / HBM roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (no sparsity)
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector, published
+CHUNK = 64
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------- algorithmic counts
+
+def algorithmic_counts(wl, n_out, n_state, keep_pseudo, with_init=True):
+    """Flops and compulsory bytes of one forward (fixed formulas that do not
+    depend on how the kernels are written).
+
+    Flops per token-head: the chunk-local products A = K K^T, P = Q K^T,
+    W = T (beta e^G K), U = T (beta V) and P Vt at 2 C d each with C = 64
+    (full C x C tiles), plus W S^T, Q S^T and the chunk-exit state update at
+    2 Dk Dv each. Tokens of draft-tree chunks (sequences of <= 64 tokens) have
+    no exit update. Bytes: q, k, v, beta, log_gate read once, the initial
+    states read once, the requested out rows, state rows and pseudo-values
+    written once. Structure arrays (parent_idx, seq_start) are read by the
+    metadata kernels and counted separately."""
+    es = 2 if wl.dtype == "bf16" else 4
+    T, H, Dk, Dv = wl.T, wl.H, wl.Dk, wl.Dv
+    lens = np.diff(wl.seq_start)
+    tree_tokens = int(lens[lens <= CHUNK].sum())
+    chain_tokens = T - tree_tokens
+    local = 2 * CHUNK * (3 * Dk + 2 * Dv)
+    flops = H * (chain_tokens * (local + 6 * Dk * Dv) + tree_tokens * (local + 4 * Dk * Dv))
+    bytes_in = T * H * (2 * Dk + Dv + 2) * es
+    bytes_init = wl.n_seq * H * Dv * Dk * 4 if with_init else 0
+    bytes_out = n_out * H * Dv * es + n_state * H * Dv * Dk * 4 + (T * H * Dv * 4 if keep_pseudo else 0)
+    bytes_struct = 4 * T + 4 * (wl.n_seq + 1)
+    return {"flops": float(flops), "bytes": float(bytes_in + bytes_init + bytes_out), "bytes_struct": float(bytes_struct)}
+
+
+def commit_counts(wl):
+    """Compulsory bytes of one gdn_tree_commit: each path reads its initial
+    state, the path's pseudo-values, keys and gates, and writes one state."""
+    es = 2 if wl.dtype == "bf16" else 4
+    H, Dk, Dv = wl.H, wl.Dk, wl.Dv
+    n_path = wl.n_path
+    L = int(wl.path_ptr[-1])
+    b = n_path * H * Dv * Dk * 4 * 2 + L * H * (Dv * 4 + Dk * es + es) + 4 * (L + 2 * n_path + 1)
+    f = L * H * 2 * Dv * Dk + n_path * H * 2 * Dv * Dk
+    return {"flops": float(f), "bytes": float(b)}
+
+
+# -------------------------------------------------------------------- traffic
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tree_forked_gated_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per walk launch from the committed rocprofv3 counter summary,
+    or None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"walk_traffic_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            kv[k.strip()] = v.strip().strip("`")
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--rotate", type=int, default=3, help="independent input sets cycled between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py runs on one GPU only: the tree-GDN path has no multi-GPU mode in this library "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    from tree_forked_gated_amd import binding as B
+    from tree_forked_gated_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    t0 = time.time()
+    wl = W.get_config(args.config)
+    log(f"workload {wl.name}: T={wl.T} H={wl.H} Dk={wl.Dk} Dv={wl.Dv} n_seq={wl.n_seq} "
+        f"({time.time() - t0:.1f} s to draw) {wl.info}")
+    cap = B.capacities(wl.parent, wl.seq_start)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+
+    def upload():
+        f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(dt).contiguous()
+        return {"q": f(wl.q), "k": f(wl.k), "v": f(wl.v), "log_gate": f(wl.log_gate), "beta": f(wl.beta),
+                "init_state": torch.from_numpy(np.ascontiguousarray(wl.init_state, np.float32)).to(dev)}
+
+    parent = torch.from_numpy(wl.parent.astype(np.int32)).to(dev)
+    seq_start = torch.from_numpy(wl.seq_start.astype(np.int32)).to(dev)
+    out_rows = None if wl.out_rows is None else torch.from_numpy(wl.out_rows.astype(np.int32)).to(dev)
+    state_rows = torch.from_numpy(wl.state_rows.astype(np.int32)).to(dev)
+    n_out = wl.T if wl.out_rows is None else int(wl.out_rows.shape[0])
+    n_state = int(wl.state_rows.shape[0])
+    is_draft = wl.path_ptr is not None
+    if is_draft:
+        pp = torch.from_numpy(wl.path_ptr.astype(np.int32)).to(dev)
+        pn = torch.from_numpy(wl.path_nodes.astype(np.int32)).to(dev)
+        ps = torch.from_numpy(wl.path_seq.astype(np.int32)).to(dev)
+
+    base = upload()
+    sets = []
+    for r in range(max(1, args.rotate)):
+        x = dict(base) if r == 0 else {k: t.clone() for k, t in base.items()}
+        dims = B.make_dims(wl.T, wl.H, wl.Dk, wl.Dv, wl.n_seq, B.GDN_BF16 if wl.dtype == "bf16" else B.GDN_F32,
+                           cap["max_forks"], cap["max_levels"])
+        x["ws"] = B.alloc_workspace(dims, dev)
+        x["out"] = torch.empty((n_out, wl.H, wl.Dv), dtype=dt, device=dev)
+        x["state_out"] = torch.empty((n_state, wl.H, wl.Dv, wl.Dk), dtype=torch.float32, device=dev)
+        x["pv"] = torch.empty((wl.T, wl.H, wl.Dv), dtype=torch.float32, device=dev) if wl.keep_pseudo else None
+        if is_draft:
+            x["cws"] = torch.empty(int(B.lib.gdn_tree_commit_workspace_size()), dtype=torch.uint8, device=dev)
+            x["committed"] = torch.empty((wl.n_path, wl.H, wl.Dv, wl.Dk), dtype=torch.float32, device=dev)
+        sets.append(x)
+    del base
+    log(f"{len(sets)} input sets resident; capacities {cap}")
+
+    def fwd(x, planned=False):
+        B.forward(x["q"], x["k"], x["v"], x["log_gate"], x["beta"], parent, seq_start, x["init_state"],
+                  out_rows=out_rows, state_rows=state_rows, keep_pseudo=wl.keep_pseudo,
+                  max_forks=cap["max_forks"], max_levels=cap["max_levels"], workspace=x["ws"], out=x["out"],
+                  state_out=x["state_out"], pseudo_v=x["pv"], stream=stream, planned=planned)
+
+    def cmt(x):
+        B.commit(x["k"], x["log_gate"], parent, seq_start, x["init_state"], x["pv"], pp, pn, ps,
+                 workspace=x["cws"], out_state=x["committed"], stream=stream)
+
+    def step(i, planned=False):
+        x = sets[i % len(sets)]
+        fwd(x, planned)
+        if is_draft and not planned:
+            cmt(x)
+
+    for i in range(len(sets)):  # plan every input set once (not a warmup step)
+        step(i)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    for x in sets:
+        B.raise_device_error(x["ws"], stream)
+    log(f"warmup {args.warmup} done")
+
+    # ---- timed region: whole steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step (events), wall {1e3 * wall / args.steps:.4f} ms/step")
+    for x in sets:
+        B.raise_device_error(x["ws"], stream)
+
+    # ---- the walk alone (metadata reused): the dominant kernel's launch duration
+    for i in range(2):
+        step(i, planned=True)
+    torch.cuda.synchronize()
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev2.record(stream)
+    for i in range(args.steps):
+        step(i, planned=True)
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    ms_walk = ev2.elapsed_time(ev3) / args.steps
+    for x in sets:
+        B.raise_device_error(x["ws"], stream)
+    ms_commit = None
+    if is_draft:
+        ev4, ev5 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev4.record(stream)
+        for i in range(args.steps):
+            cmt(sets[i % len(sets)])
+        ev5.record(stream)
+        torch.cuda.synchronize()
+        ms_commit = ev4.elapsed_time(ev5) / args.steps
+    log(f"walk only: {ms_walk:.4f} ms/launch-set ({cap['max_levels']} level launches)"
+        + (f"; commit {ms_commit:.4f} ms" if ms_commit is not None else ""))
+
+    cnt = algorithmic_counts(wl, n_out, n_state, wl.keep_pseudo)
+    walk_gbs = cnt["bytes"] / (ms_walk * 1e-3) / 1e9
+    walk_tflops = cnt["flops"] / (ms_walk * 1e-3) / 1e12
+    ai = cnt["flops"] / cnt["bytes"]
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = measured_traffic(wl.name)
+    if ai < ridge or wl.dtype != "bf16":
+        roof = {"bound": "hbm", "achieved": round(walk_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(walk_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(walk_tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(walk_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
+    roof.update({"kernel": "k_walk", "launches_per_step": cap["max_levels"], "ms_per_step": round(ms_walk, 5),
+                 "alg_bytes": cnt["bytes"], "alg_flops": cnt["flops"],
+                 "mfma_frac": round(walk_tflops / BF16_PEAK_TFLOPS, 4),
+                 "hbm_frac": round(walk_gbs / HBM_PEAK_GBS, 4)})
+
+    # ---- parity of the timed outputs (set 0 holds the last step that used it) and the CPU baseline
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle  # the CPU baseline leg: the oracle as it stands
+        oracle.build(force=False)
+        threads = args.cpu_threads or min(16, oracle.default_threads())
+        t0 = time.perf_counter()
+        ref = oracle.forward(wl, "f32", n_threads=threads, keep_pseudo=wl.keep_pseudo)
+        refc = oracle.commit(wl, "f32", n_threads=threads) if is_draft else None
+        cpu_s = time.perf_counter() - t0
+        cpu = {"value": round(wl.T / cpu_s, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"whole {wl.name} workload ({wl.T} tokens x {wl.H} heads), fp32 per-token parent walk"
+                         + (" + replay commit" if is_draft else "") + f", {cpu_s:.2f} s wall"}
+        log(f"cpu baseline: {cpu_s:.2f} s on {threads} threads")
+        x = sets[0]
+        step(0)
+        torch.cuda.synchronize()
+
+        def rel(a, b):
+            a = np.asarray(a, np.float64)
+            b = np.asarray(b, np.float64)
+            return float(np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-30))
+
+        ref_out = ref["out"] if wl.out_rows is None else ref["out"][wl.out_rows]
+        parity = {"out": rel(x["out"].float().cpu().numpy(), ref_out)}
+        if n_state:
+            parity["state"] = rel(x["state_out"].cpu().numpy(), ref["state"])
+        if is_draft:
+            parity["commit"] = rel(x["committed"].cpu().numpy(), refc)
+        parity = {k: float(f"{v:.3e}") for k, v in parity.items()}
+        parity["tol"] = 1e-2 if wl.dtype == "bf16" else 1e-4
+        parity["ok"] = all(v <= parity["tol"] for k, v in parity.items() if k not in ("tol",))
+        log(f"parity vs oracle: {parity}")
+
+    value = wl.T / (ms_step * 1e-3)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.T, "heads": wl.H, "d_k": wl.Dk, "d_v": wl.Dv,
+                   "sequences": wl.n_seq, "chunk": CHUNK, "state_dtype": "f32", "structure": wl.info.get("structure"),
+                   "parallelism": "single GPU", "input_sets_rotated": len(sets)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+    }
+    if ms_commit is not None:
+        cc = commit_counts(wl)
+        line["commit"] = {"ms": round(ms_commit, 5), "alg_bytes": cc["bytes"],
+                          "hbm_frac": round(cc["bytes"] / (ms_commit * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
