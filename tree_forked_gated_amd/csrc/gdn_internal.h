@@ -79,6 +79,10 @@ bool walk_supported(int dtype, int dk, int bv);
 bool walk_mfma_supported(int dtype, int dk, int bv);
 bool walk_mfma_fits(const gdn_tree_dims& d);  // sizes within its 32-bit offsets
 hipError_t launch_walk_mfma(const gdn_tree_fwd_args& a, const Meta& m, int bv, hipStream_t s);
+// pipelined MFMA walk (state waves + helper waves), same coverage
+bool walk_pipe_supported(int dtype, int dk, int bv);
+bool walk_pipe_fits(const gdn_tree_dims& d);
+hipError_t launch_walk_pipe(const gdn_tree_fwd_args& a, const Meta& m, int bv, hipStream_t s);
 int walk_lds_bytes(int dtype, int dk, int bv);
 
 }  // namespace gdn

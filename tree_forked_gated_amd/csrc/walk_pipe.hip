@@ -1,0 +1,953 @@
+// Chunked tree-WY walk for bf16 inputs with d_k = 128 on gfx950: a software
+// pipeline over chunks with specialised waves.
+//
+// Per chunk of n <= 64 tokens with entry state S_e (d_v x d_k), chunk-local
+// path sums of log gates G and ancestor-or-self mask M (TreeWY, "Speculative
+// Verification for Gated DeltaNet Hybrids", section 3: "Key rewrite", Eq. 2
+// "Verifying a draft" and Eq. 3 "Reconstruct on commit"):
+//
+//   A[i][j] = beta_i exp(G_i - G_j) (k_i . k_j)   j a strict ancestor of i
+//   R       = diag(beta) (V - diag(e^G) K S_e^T)   right-hand side of Eq. 2
+//   (I + A) Vt = R                                  pseudo-values, one per token
+//   O       = diag(e^G) Q S_e^T + (M . exp(G_i - G_j) . Q K^T) Vt
+//   S_a     = e^{G_a} S_e + sum over j ancestor-or-self of a of exp(G_a - G_j) vt_j k_j^T
+//
+// Eq. 2 is solved by blocks of 16 tokens: the four 16 x 16 diagonal blocks of
+// I + A are inverted in fp32, and Vt_b = (I + A_bb)^{-1} (R_b - sum over m < b
+// of A_bm Vt_m).
+//
+// Only the products with S_e depend on the previous chunk. A workgroup walks
+// one (segment, head, d_v tile) item after another and splits each chunk's
+// work by that line:
+//
+// * state waves (one per 16 columns of the d_v tile) hold their rows of S in
+//   fp32 registers and do everything that involves S: K S_e^T, R, the block
+//   substitution, Q S_e^T and P Vt, the outputs and pseudo-values, and the
+//   states after requested tokens and at the chunk exit;
+// * two helper waves work one chunk ahead: from that chunk's K and Q they form
+//   the A tiles, the inverses of the diagonal blocks and the masked, decayed
+//   P = M . exp . Q K^T, and leave them in LDS as ready MFMA operands. They
+//   also copy q and k two chunks ahead and v one chunk ahead from HBM into LDS
+//   (direct-to-LDS loads), and the second helper walks the item list and
+//   prepares each chunk's token tables.
+//
+// One barrier per chunk separates the stages. The state is kept transposed in
+// the MFMA accumulator layout, with its d_k index permuted so that the
+// accumulators, converted to bf16, are directly the B operands of K S_e^T and
+// Q S_e^T; the update takes its K^T operand with transposing LDS reads.
+//
+// Reduction orders depend only on the chunk's own tokens (never on the d_v
+// tile width, the grid or other items), so results are bitwise independent of
+// the batch around a sequence and of the d_v tile.
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int DK = 128;
+constexpr int kXcd = kWalkQueues;  // workgroup b runs on XCD b % 8 of an MI355X
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Token tables of one chunk (byte offsets): 64 entries each.
+constexpr int tG2 = 0;      // float G log2(e)
+constexpr int tEG = 256;    // float exp(G)
+constexpr int tB = 512;     // float beta
+constexpr int tDX = 768;    // float exp(G_{n-1} - G_j) for j < n, else 0 (decay to the chunk exit)
+constexpr int tMl = 1024;   // u32 ancestor-or-self mask, tokens 0..31
+constexpr int tMh = 1280;   // u32 same, tokens 32..63
+constexpr int tOR = 1536;   // int output row or -1
+constexpr int tFS = 1792;   // int fork slot or -1
+constexpr int tSR = 2048;   // int state row or -1
+constexpr int tD = 2304;    // chunk descriptor
+constexpr int kTB = 2368;
+
+// Products of one chunk, laid out as per-lane MFMA operands (byte offsets).
+constexpr int pNA = 0;              // 6 blocks x 64 lanes x 8 B: -A_bm (m < b), 16x16x16 A operands
+constexpr int kDIS = 640;           // stride between diagonal inverses (512 B used)
+constexpr int pDI = 3072;           // 4 blocks: (I + A_bb)^{-1}, 16x16x16 A operands
+constexpr int pP = pDI + 4 * kDIS;  // 6 pairs x 64 lanes x 16 B: P row block x 32 tokens, 16x16x32 A operands
+constexpr int kPR = pP + 6 * 1024;
+// fp32 staging of one helper's diagonal blocks of A, transposed: [4][16][kLTR] + pad
+constexpr int kLTR = 20;
+constexpr int kLTS = 16 * kLTR + 4;
+
+template <int BV>
+struct Cfg {
+  static constexpr int NB = 1;                 // 16-column blocks per state wave
+  static constexpr int NS = BV / (16 * NB);    // state waves
+  static constexpr int NW = NS + 2;            // plus two helpers
+  static constexpr int NTHR = 64 * NW;
+  static constexpr int VPR = BV / 8;    // 16-byte pieces per V row
+  static constexpr int RPI = 64 / VPR;  // V rows per direct-to-LDS instruction
+  static constexpr int VT = 64 * BV * 2;
+  static constexpr int oKQ = 0;                  // [3] K tile (16 KB) then Q tile (16 KB)
+  static constexpr int oTB = oKQ + 3 * 32768;    // [3] token tables
+  static constexpr int oV = oTB + 3 * kTB;       // [2] V tiles bf16 [64][BV]
+  static constexpr int oPR = oV + 2 * VT;        // [2] products
+  static constexpr int oLT = oPR + 2 * kPR;      // diagonal-block staging
+  static constexpr int oND = oLT + 4 * kLTS * 4; // [2] descriptors of chunks to copy, by parity
+  static constexpr int bytes = oND + 128;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static_assert(oTB % 16 == 0 && oV % 16 == 0 && oPR % 16 == 0 && oLT % 16 == 0 && oND % 16 == 0, "alignment");
+};
+
+struct Desc {
+  int valid;         // 0: no chunk (the walk is over)
+  int t0, n;         // first token, tokens in the chunk
+  int h, v0;         // head, first column of the d_v tile
+  int mode;          // 1: tree chunk (a whole sequence of <= 64 tokens)
+  int sq;            // sequence
+  int first;         // first chunk of its item: the state waves load the entry state
+  int need_exit;     // the chunk-exit state feeds a next chunk of the same segment
+  int has_out;       // some token of the chunk has an output row
+  unsigned req_lo, req_hi;  // tokens whose state is asked for (fork slot or state row)
+  const float* sin;  // entry state rows of this tile (row v0), or null for zeros
+  int pad[2];
+};
+static_assert(sizeof(Desc) <= 64, "descriptor");
+
+struct Args {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* g;
+  const __bf16* b;
+  const int* parent;
+  const float* init;
+  __bf16* out;
+  float* state_out;
+  float* pv;
+  float* fork_states;
+  const int4* unit_info;
+  const int* out_map;
+  const int* state_map;
+  const int* fork_slot;
+  const unsigned long long* tree_mask;
+  const unsigned long long* err;
+  const int* level_count;
+  const int* level_ptr;
+  int H, Dv, NT, level, out_all;
+};
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// 16 bytes per lane from global memory (sbase + voff) straight into LDS: lane
+// i's bytes land at lds_base + 16 i. Issued as inline assembly so that the
+// compiler does not treat the copy as a pending write to all of LDS (it would
+// otherwise wait for it before every LDS access); completion is awaited
+// explicitly with wait_vm(). M0 holds the LDS base for the instruction; nothing
+// else in this kernel uses M0.
+__device__ __forceinline__ void dma16(const void* sbase, unsigned voff, const void* lds_base) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((const lds_void*)lds_base));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(voff), "s"(sbase)
+               : "memory");
+}
+
+// 16-byte piece p of row r of a K or Q tile sits at slot p ^ kq_swz(r).
+__device__ __forceinline__ int kq_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// V rows of 8 pieces (d_v tile of 64) are permuted too; narrower rows need not be.
+template <int BV>
+__device__ __forceinline__ int v_swz(int r) { return BV == 64 ? ((r & 3) << 1) : 0; }
+
+__device__ __forceinline__ i16x4 tr_read(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 cat8(i16x4 lo, i16x4 hi) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 cat8b(bf16x4 lo, bf16x4 hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
+
+__device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
+  bf16x4 r;
+  r[0] = (__bf16)x[0];
+  r[1] = (__bf16)x[1];
+  r[2] = (__bf16)x[2];
+  r[3] = (__bf16)x[3];
+  return r;
+}
+
+__device__ __forceinline__ float bf_up(unsigned short x) { return __uint_as_float((unsigned)x << 16); }
+
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0); }
+
+template <typename T>
+__device__ __forceinline__ T lds_at(const unsigned char* base, int byte_off) {
+  return *reinterpret_cast<const T*>(base + byte_off);
+}
+
+__device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// --------------------------------------------------------------- item feed
+// The second helper walks the level's items in a fixed order: the workgroups
+// of one XCD share the units (segment, head) whose index is congruent to the
+// XCD mod 8, so all d_v tiles of a unit read its q and k through the same L2,
+// and the k-th workgroup of the XCD takes the XCD's items k, k + G, k + 2 G,
+// ... (G workgroups per XCD). The unit record of the next item is loaded
+// while the current one is walked.
+
+struct Feed {
+  int start, len, mode, sq, slot, h, tile, nch, c;
+  bool cur;     // an item is being walked
+  int li;       // XCD-local index of the next item to start
+  int4 info_v;  // unit record of that item (in flight until the next vmcnt(0))
+  bool nx_valid;
+};
+
+// Unit indices stay below count * H <= T * H < 2^31 (checked on the host).
+__device__ __forceinline__ void feed_prefetch(Feed& f, const Args& a, int xcd, int count, int base) {
+  const unsigned u = (unsigned)xcd + (unsigned)kXcd * ((unsigned)f.li / (unsigned)a.NT);
+  f.nx_valid = u < (unsigned)count * (unsigned)a.H;
+  f.info_v = make_int4(0, 0, 0, -1);
+  if (f.nx_valid) f.info_v = a.unit_info[base + (int)(u / (unsigned)a.H)];
+}
+
+// The descriptor of the next chunk to load (valid = 0 when the level is done).
+// Reads the prefetched unit record: call it only after a vmcnt(0).
+template <int BV>
+__device__ __forceinline__ Desc feed_next(Feed& f, const Args& a, int xcd, int count, int base, int per_xcd) {
+  Desc d;
+  d.valid = 0;
+  if (!(f.cur && f.c < f.nch)) {
+    f.cur = false;
+    if (!f.nx_valid) return d;
+    const unsigned u = (unsigned)xcd + (unsigned)kXcd * ((unsigned)f.li / (unsigned)a.NT);
+    f.start = rfl(f.info_v.x);
+    f.len = rfl(f.info_v.y);
+    const int ms = rfl(f.info_v.z);
+    f.mode = ms & 1;
+    f.sq = ms >> 1;
+    f.slot = rfl(f.info_v.w);
+    f.h = (int)(u % (unsigned)a.H);
+    f.tile = (int)((unsigned)f.li % (unsigned)a.NT);
+    f.nch = f.mode ? 1 : (f.len + kChunk - 1) / kChunk;
+    f.c = 0;
+    f.cur = true;
+    f.li += per_xcd;
+    feed_prefetch(f, a, xcd, count, base);
+  }
+  const size_t SS = (size_t)a.Dv * DK;
+  d.valid = 1;
+  d.t0 = f.start + f.c * kChunk;
+  d.n = min(kChunk, f.len - f.c * kChunk);
+  d.h = f.h;
+  d.v0 = f.tile * BV;
+  d.mode = f.mode;
+  d.sq = f.sq;
+  d.first = f.c == 0;
+  d.need_exit = (!f.mode) && (f.c + 1 < f.nch);
+  d.has_out = 0;
+  d.req_lo = d.req_hi = 0;
+  d.sin = nullptr;
+  if (d.first) {
+    const float* s = f.slot >= 0 ? a.fork_states + ((size_t)f.slot * a.H + f.h) * SS
+                                 : (a.init ? a.init + ((size_t)f.sq * a.H + f.h) * SS : nullptr);
+    d.sin = s ? s + (size_t)d.v0 * DK : nullptr;
+  }
+  f.c += 1;
+  return d;
+}
+
+// A descriptor read from LDS, with every field made wave-uniform.
+__device__ __forceinline__ Desc uniform_desc(const Desc& s) {
+  Desc d;
+  d.valid = rfl(s.valid);
+  d.t0 = rfl(s.t0);
+  d.n = rfl(s.n);
+  d.h = rfl(s.h);
+  d.v0 = rfl(s.v0);
+  d.mode = rfl(s.mode);
+  d.sq = rfl(s.sq);
+  d.first = rfl(s.first);
+  d.need_exit = rfl(s.need_exit);
+  d.has_out = rfl(s.has_out);
+  d.req_lo = (unsigned)rfl((int)s.req_lo);
+  d.req_hi = (unsigned)rfl((int)s.req_hi);
+  const unsigned long long p = (unsigned long long)s.sin;
+  d.sin = (const float*)(((unsigned long long)(unsigned)rfl((int)(p >> 32)) << 32) | (unsigned)rfl((int)p));
+  return d;
+}
+
+__device__ __forceinline__ void put_desc(unsigned char* p, const Desc& d, int lane) {
+  if (lane == 0) *reinterpret_cast<Desc*>(p) = d;
+}
+
+// ------------------------------------------------------------ chunk loads
+
+// Helper hid's share of the direct-to-LDS copies of the K and Q rows of chunk
+// d into slot kq (K at +0, Q at +16384). Rows at or beyond d.n are zero-filled.
+__device__ __forceinline__ void issue_kq(const Args& a, const Desc& d, unsigned char* kq, int hid, int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const bool full = d.n == kChunk;
+  // row 4 blk + g4, slot l16 holds piece l16 ^ kq_swz(row)
+  const unsigned row0 = (((unsigned)d.t0 + g4) * (unsigned)a.H + d.h) * (DK * 2);
+  const unsigned step = 4u * a.H * (DK * 2);  // bytes per instruction (4 rows)
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int ins = 2 * j + hid;
+    const bool isK = ins < 16;
+    const int blk = ins & 15;
+    const int row = 4 * blk + g4;
+    unsigned char* dst = kq + (isK ? 0 : 16384) + blk * 1024;
+    const unsigned char* sbase = reinterpret_cast<const unsigned char*>(isK ? a.k : a.q) + (size_t)blk * step;
+    const unsigned voff = row0 + (unsigned)((l16 ^ ((g4 << 2) | (blk & 3))) * 16);
+    if (full || row < d.n) dma16(sbase, voff, dst);
+    else *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Helper hid's share of the copies of the V tile of chunk d into vb.
+template <int BV>
+__device__ __forceinline__ void issue_v(const Args& a, const Desc& d, unsigned char* vb, int hid, int lane) {
+  using C = Cfg<BV>;
+  const bool full = d.n == kChunk;
+  // row ins * RPI + lane / VPR, slot lane % VPR
+  const int vr = lane / C::VPR, vs = lane % C::VPR;
+  const unsigned row0 = (((unsigned)d.t0 + vr) * (unsigned)a.H + d.h) * (unsigned)(a.Dv * 2) + (unsigned)d.v0 * 2 +
+                        (unsigned)((vs ^ v_swz<BV>(vr)) * 16);
+  const unsigned step = (unsigned)C::RPI * a.H * (a.Dv * 2);
+#pragma unroll
+  for (int ins = 0; ins < C::VPR; ++ins) {
+    if ((ins & 1) != hid) continue;
+    const int row = ins * C::RPI + vr;
+    unsigned char* dst = vb + ins * 1024;
+    const unsigned char* sbase = reinterpret_cast<const unsigned char*>(a.v) + (size_t)ins * step;
+    if (full || row < d.n) dma16(sbase, row0, dst);
+    else *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Raw per-token values of a chunk (one token per lane), converted only after
+// the wait that follows the copies so that no compiler wait lands among them.
+struct TokenRegs {
+  unsigned short g, b;  // bf16 bits
+  int par, om, sm, fs;
+};
+
+__device__ __forceinline__ TokenRegs load_tokens(const Args& a, const Desc& d, int lane) {
+  TokenRegs r;
+  r.g = 0;
+  r.b = 0;
+  r.par = -1;
+  r.om = kUnmapped;
+  r.sm = kUnmapped;
+  r.fs = -1;
+  if (d.valid && lane < d.n) {
+    const int t = d.t0 + lane;
+    r.g = reinterpret_cast<const unsigned short*>(a.g)[(size_t)t * a.H + d.h];
+    r.b = reinterpret_cast<const unsigned short*>(a.b)[(size_t)t * a.H + d.h];
+    if (d.mode) r.par = a.parent[t];
+    r.om = a.out_all ? t : a.out_map[t];
+    r.sm = a.state_map[t];
+    r.fs = a.fork_slot[t];
+  }
+  return r;
+}
+
+// Token tables of chunk d into tb (second helper).
+__device__ __forceinline__ void store_tokens(const Args& a, Desc d, const TokenRegs& r, unsigned char* tb, int lane) {
+  if (!d.valid) {
+    put_desc(tb + tD, d, lane);
+    return;
+  }
+  // chunk-local path sums of log gates: a prefix sum on a chain, pointer
+  // jumping over in-chunk parents in a tree chunk (six rounds cover 64 levels)
+  const int i = lane;
+  const bool valid = i < d.n;
+  float G = bf_up(r.g);
+  unsigned long long mask;
+  if (d.mode) {
+    int pj = (valid && r.par >= d.t0 && r.par < d.t0 + i) ? r.par - d.t0 : -1;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int src = pj >= 0 ? pj : i;
+      const float pG = __shfl(G, src);
+      const int pp = __shfl(pj, src);
+      if (pj >= 0) {
+        G += pG;
+        pj = pp;
+      }
+    }
+    mask = a.tree_mask[(size_t)d.sq * kChunk + i];
+  } else {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(G, off);
+      if (i >= off) G += o;
+    }
+    mask = (i == 63) ? ~0ull : ((2ull << i) - 1ull);
+  }
+  const float g2 = G * kLog2e;
+  const float g2last = __shfl(g2, d.n - 1);
+  const int orow = (valid && r.om != kUnmapped) ? r.om : -1;
+  const int fs = valid ? r.fs : -1;
+  const int sr = (valid && r.sm != kUnmapped) ? r.sm : -1;
+  reinterpret_cast<float*>(tb + tG2)[i] = g2;
+  reinterpret_cast<float*>(tb + tEG)[i] = __expf(G);
+  reinterpret_cast<float*>(tb + tB)[i] = bf_up(r.b);
+  reinterpret_cast<float*>(tb + tDX)[i] = valid ? __builtin_amdgcn_exp2f(g2last - g2) : 0.f;
+  reinterpret_cast<unsigned*>(tb + tMl)[i] = (unsigned)mask;
+  reinterpret_cast<unsigned*>(tb + tMh)[i] = (unsigned)(mask >> 32);
+  reinterpret_cast<int*>(tb + tOR)[i] = orow;
+  reinterpret_cast<int*>(tb + tFS)[i] = fs;
+  reinterpret_cast<int*>(tb + tSR)[i] = sr;
+  const unsigned long long rq = __ballot(fs >= 0 || sr >= 0);
+  d.has_out = __ballot(orow >= 0) != 0ull;
+  d.req_lo = (unsigned)rq;
+  d.req_hi = (unsigned)(rq >> 32);
+  put_desc(tb + tD, d, lane);
+}
+
+// ---------------------------------------------------------------- helpers
+
+// The S-independent operands of one chunk. Helper 0 takes the tiles of token
+// row blocks 0..2, helper 1 those of row block 3; each inverts its own
+// diagonal blocks. The Gram and Q K^T tiles are computed with K of the column
+// block as the A operand, so that the accumulator of tile (row block b,
+// column block m) holds row 16 b + l16, columns 16 m + 4 g4 .. + 3: exactly the
+// A-operand layout the state waves read.
+template <int HID, bool HAS_OUT>
+__device__ __forceinline__ void products(const unsigned char* kq, const unsigned char* tb, unsigned char* pr, float* lt,
+                                         bool tree, int lane) {
+  constexpr int R0 = HID == 0 ? 0 : 3, R1 = HID == 0 ? 3 : 4;  // token row blocks [R0, R1)
+  const int g4 = lane >> 4, l16 = lane & 15;
+  int oF[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) oF[ks] = l16 * 256 + (((4 * ks + g4) ^ kq_swz(l16)) << 4);
+  bf16x8 KF[4][4];
+#pragma unroll
+  for (int b = 0; b < R1; ++b)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) KF[b][ks] = lds_at<bf16x8>(kq + oF[ks], b * 4096);
+  const float* G2 = reinterpret_cast<const float*>(tb + tG2);
+  const float* Bt = reinterpret_cast<const float*>(tb + tB);
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int rb = R0; rb < R1; ++rb) {
+    bf16x8 QF[4];
+    if (HAS_OUT) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) QF[ks] = lds_at<bf16x8>(kq + 16384 + oF[ks], rb * 4096);
+    }
+    const int i = 16 * rb + l16;
+    const float g2i = G2[i], bi = Bt[i];
+    const unsigned mw0 = reinterpret_cast<const unsigned*>(tb + tMl)[i];
+    const unsigned mw1 = reinterpret_cast<const unsigned*>(tb + tMh)[i];
+#pragma unroll
+    for (int cb = 0; cb <= rb; ++cb) {
+      f32x4 ga = zero, gp = zero;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) ga = mma32(KF[cb][ks], KF[rb][ks], ga);
+      if (HAS_OUT) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) gp = mma32(KF[cb][ks], QF[ks], gp);
+      }
+      const float4 gj4 = *reinterpret_cast<const float4*>(G2 + 16 * cb + 4 * g4);
+      const float gj[4] = {gj4.x, gj4.y, gj4.z, gj4.w};
+      // decay exp(G_i - G_j) where token j is an ancestor-or-self of token i, else 0
+      float e[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jl = 4 * g4 + r;  // j = 16 cb + jl
+        const bool in_tree = ((cb >= 2 ? mw1 : mw0) >> ((16 * cb + jl) & 31)) & 1u;
+        const bool anc = tree ? in_tree : (cb < rb || jl <= l16);
+        e[r] = anc ? __builtin_amdgcn_exp2f(g2i - gj[r]) : 0.f;
+      }
+      if (cb < rb) {
+        bf16x4 na;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) na[r] = (__bf16)(-(bi * e[r] * ga[r]));
+        *reinterpret_cast<bf16x4*>(pr + pNA + ((rb * (rb - 1)) / 2 + cb) * 512 + lane * 8) = na;
+      } else {
+        // strict lower part of the diagonal block, transposed: lt[rb][j][i]
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          lt[rb * kLTS + (4 * g4 + r) * kLTR + l16] = (4 * g4 + r != l16) ? bi * e[r] * ga[r] : 0.f;
+      }
+      if (HAS_OUT) {
+        bf16x4 pv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv[r] = (__bf16)(e[r] * gp[r]);
+        const int pair = (rb <= 1 ? rb : 2 * rb - 2) + (cb >> 1);
+        *reinterpret_cast<bf16x4*>(pr + pP + pair * 1024 + lane * 16 + (cb & 1) * 8) = pv;
+      }
+    }
+  }
+  wait_lds();
+  // Row c = l16 of (I + L)^{-1} for the diagonal block g4, by back substitution
+  // on the transposed system (I + L)^T z = e_c, in fp32.
+  if (g4 >= R0 && g4 < R1) {
+    const float* L = lt + g4 * kLTS;  // L[r * kLTR + c'] = A[c'][r] of the block
+    float z[16];
+#pragma unroll
+    for (int r = 15; r >= 0; --r) {
+      float acc = (r == l16) ? 1.f : 0.f;
+#pragma unroll
+      for (int c = r + 1; c < 16; ++c) acc -= L[r * kLTR + c] * z[c];
+      z[r] = acc;
+    }
+    unsigned char* d = pr + pDI + g4 * kDIS;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x4 v;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) v[y] = (__bf16)z[4 * q + y];
+      *reinterpret_cast<bf16x4*>(d + (q * 16 + l16) * 8) = v;
+    }
+  }
+}
+
+__device__ __forceinline__ void chunk_products(int hid, const Desc& c, const unsigned char* kq, const unsigned char* tb,
+                                      unsigned char* pr, float* lt, int lane) {
+  const bool tree = c.mode != 0;
+  if (hid == 0) {
+    if (c.has_out) products<0, true>(kq, tb, pr, lt, tree, lane);
+    else products<0, false>(kq, tb, pr, lt, tree, lane);
+  } else {
+    if (c.has_out) products<1, true>(kq, tb, pr, lt, tree, lane);
+    else products<1, false>(kq, tb, pr, lt, tree, lane);
+  }
+}
+
+template <int BV>
+__device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, int hid, int lane, Feed& f, int xcd, int count,
+                            int base, int per_xcd) {
+  using C = Cfg<BV>;
+  Desc* nds = reinterpret_cast<Desc*>(smem + C::oND);
+  float* lt = reinterpret_cast<float*>(smem + C::oLT);
+  TokenRegs tr;
+  // Iteration -1 forms the products of chunk 0 while the state waves wait.
+  for (int it = -1;; ++it) {
+    if (it >= 0 && !rfl(reinterpret_cast<const Desc*>(smem + C::oTB + (it % 3) * kTB + tD)->valid)) break;
+    const int s1 = (it + 1) % 3, s2 = (it + 2) % 3;
+    unsigned char* tb1 = smem + C::oTB + s1 * kTB;
+    const Desc nd = uniform_desc(nds[it & 1]);                              // chunk it + 2: copy K, Q
+    const Desc nx = uniform_desc(*reinterpret_cast<const Desc*>(tb1 + tD));  // chunk it + 1: copy V, products
+    if (hid == 1) tr = load_tokens(a, nd, lane);
+    if (nd.valid) issue_kq(a, nd, smem + C::oKQ + s2 * 32768, hid, lane);
+    if (nx.valid) issue_v<BV>(a, nx, smem + C::oV + ((it + 1) & 1) * C::VT, hid, lane);
+    if (nx.valid) chunk_products(hid, nx, smem + C::oKQ + s1 * 32768, tb1, smem + C::oPR + ((it + 1) & 1) * kPR, lt, lane);
+    wait_vm();  // this wave's copies, token values and unit record have landed
+    if (hid == 1) {
+      Desc nn;
+      nn.valid = 0;
+      if (nd.valid) nn = feed_next<BV>(f, a, xcd, count, base, per_xcd);
+      put_desc(reinterpret_cast<unsigned char*>(nds + ((it + 1) & 1)), nn, lane);
+      store_tokens(a, nd, tr, smem + C::oTB + s2 * kTB, lane);
+    }
+    lds_barrier();
+  }
+}
+
+// ------------------------------------------------------------ state waves
+
+// Per-lane LDS offsets of a state wave.
+struct SOff {
+  int F[4];   // row fragment of K or Q rows 0..15, 16 B per lane (row block rb adds 4096 rb)
+  int KT[8];  // transposed read of K rows 4 g4 + l16/4 for state block dt (rows + 16 add 4096)
+  int V;      // transposed read of V rows 4 g4 + l16/4, the wave's 16 columns (row block rb adds 32 BV rb)
+};
+
+// One chunk on a state wave: K S_e^T, R, the block substitution, the outputs
+// and pseudo-values, then the states after requested tokens and at the exit.
+// ST[dt] (dt = 2 m + bb) holds S^T of the wave's columns in the accumulator
+// layout, lane (l16, g4) holding S[col][32 m + 8 g4 + 4 bb + r]; Sb[m] is its
+// bf16 B operand for d_k 32 m .. 32 m + 31 in natural k order.
+template <int BV, bool HAS_OUT>
+__device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* tb, const unsigned char* kq,
+                                            const unsigned char* vt, const unsigned char* pr, const SOff& o,
+                                            f32x4 (&ST)[8], bf16x8 (&Sb)[4], int t0, int n, int h, int v0w, int mode,
+                                            bool need_exit, unsigned long long todo, int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const unsigned HDv = (unsigned)a.H * a.Dv;
+  const unsigned hcol = (unsigned)h * a.Dv + (unsigned)(v0w + l16);  // column within a token row of out / pv
+  const float* sEG = reinterpret_cast<const float*>(tb + tEG);
+  const float* sB = reinterpret_cast<const float*>(tb + tB);
+
+  // K S_e^T and Q S_e^T for the wave's columns
+  f32x4 X[4], O[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    bf16x8 KF[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) KF[m] = lds_at<bf16x8>(kq + o.F[m], rb * 4096);
+    X[rb] = zero;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) X[rb] = mma32(KF[m], Sb[m], X[rb]);
+  }
+  if (HAS_OUT) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      bf16x8 QF[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) QF[m] = lds_at<bf16x8>(kq + 16384 + o.F[m], rb * 4096);
+      O[rb] = zero;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) O[rb] = mma32(QF[m], Sb[m], O[rb]);
+    }
+  }
+  // R = beta (V - e^G K S^T) in place of X, and the e^G Q S^T part of O
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const float4 eg = *reinterpret_cast<const float4*>(sEG + 16 * rb + 4 * g4);
+    const float4 bi = *reinterpret_cast<const float4*>(sB + 16 * rb + 4 * g4);
+    const bf16x4 vb = __builtin_bit_cast(bf16x4, tr_read(vt + o.V + rb * 32 * BV));
+    X[rb][0] = bi.x * ((float)vb[0] - eg.x * X[rb][0]);
+    X[rb][1] = bi.y * ((float)vb[1] - eg.y * X[rb][1]);
+    X[rb][2] = bi.z * ((float)vb[2] - eg.z * X[rb][2]);
+    X[rb][3] = bi.w * ((float)vb[3] - eg.w * X[rb][3]);
+    if (HAS_OUT) {
+      O[rb][0] *= eg.x;
+      O[rb][1] *= eg.y;
+      O[rb][2] *= eg.z;
+      O[rb][3] *= eg.w;
+    }
+  }
+  // block substitution with the helpers' -A_bm and (I + A_bb)^{-1}
+  bf16x4 nA[6], DI[4];
+#pragma unroll
+  for (int k = 0; k < 6; ++k) nA[k] = lds_at<bf16x4>(pr + pNA + k * 512, lane * 8);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) DI[b] = lds_at<bf16x4>(pr + pDI + b * kDIS, lane * 8);
+  f32x4 Vt[4];
+  bf16x4 Vb[4];
+  {
+    Vt[0] = mma16(DI[0], to_bf4(X[0]), zero);
+    Vb[0] = to_bf4(Vt[0]);
+    f32x4 y = mma16(nA[0], Vb[0], X[1]);
+    Vt[1] = mma16(DI[1], to_bf4(y), zero);
+    Vb[1] = to_bf4(Vt[1]);
+    y = mma16(nA[1], Vb[0], X[2]);
+    y = mma16(nA[2], Vb[1], y);
+    Vt[2] = mma16(DI[2], to_bf4(y), zero);
+    Vb[2] = to_bf4(Vt[2]);
+    y = mma16(nA[3], Vb[0], X[3]);
+    y = mma16(nA[4], Vb[1], y);
+    y = mma16(nA[5], Vb[2], y);
+    Vt[3] = mma16(DI[3], to_bf4(y), zero);
+    Vb[3] = to_bf4(Vt[3]);
+  }
+  if (HAS_OUT) {
+    // O += P Vt over pairs of 16-token blocks (blocks of P above the diagonal are zero)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+      for (int mp = 0; mp < 2; ++mp) {
+        if (2 * mp > rb) continue;
+        const int pair = (rb <= 1 ? rb : 2 * rb - 2) + mp;
+        const bf16x8 pa = lds_at<bf16x8>(pr + pP + pair * 1024, lane * 16);
+        O[rb] = mma32(pa, cat8b(Vb[2 * mp], Vb[2 * mp + 1]), O[rb]);
+      }
+    }
+    if (a.out_all && n == kChunk) {  // every token of a full chunk is an output row, in stream order
+      __bf16* ob = a.out + ((unsigned)t0 + 4 * g4) * HDv + hcol;
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ob[(16 * rb + r) * HDv] = (__bf16)O[rb][r];
+    } else {
+      const int* sOR = reinterpret_cast<const int*>(tb + tOR);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int4 orow = *reinterpret_cast<const int4*>(sOR + 16 * rb + 4 * g4);
+        const int ors[4] = {orow.x, orow.y, orow.z, orow.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (ors[r] >= 0) a.out[(unsigned)ors[r] * HDv + hcol] = (__bf16)O[rb][r];
+      }
+    }
+  }
+  if (a.pv) {
+    float* pvb = a.pv + ((unsigned)t0 + 4 * g4) * HDv + hcol;
+    if (n == kChunk) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pvb[(16 * rb + r) * HDv] = Vt[rb][r];
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * rb + 4 * g4 + r < n) pvb[(16 * rb + r) * HDv] = Vt[rb][r];
+    }
+  }
+  // states after requested tokens (fork slots, state rows) and at the chunk exit
+  if (!todo) return;
+  const float* sG2 = reinterpret_cast<const float*>(tb + tG2);
+  const size_t SS = (size_t)a.Dv * DK;
+  do {
+    const int p = __builtin_ctzll(todo);
+    todo &= todo - 1ull;
+    // masked, decayed pseudo-values exp(G_p - G_j) vt_j for j ancestor-or-self of p
+    // (zero past p, so the product over tokens 32..63 adds nothing when p < 32);
+    // on a chain the last token takes the exit decay table (zero past n)
+    bf16x4 Wb[4];
+    if (!mode && p == n - 1) {
+      const float* sDX = reinterpret_cast<const float*>(tb + tDX);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const float4 dx = *reinterpret_cast<const float4*>(sDX + 16 * mb + 4 * g4);
+        f32x4 wv;
+        wv[0] = Vt[mb][0] * dx.x;
+        wv[1] = Vt[mb][1] * dx.y;
+        wv[2] = Vt[mb][2] * dx.z;
+        wv[3] = Vt[mb][3] * dx.w;
+        Wb[mb] = to_bf4(wv);
+      }
+    } else {
+      const unsigned mlo = reinterpret_cast<const unsigned*>(tb + tMl)[p];
+      const unsigned mhi = reinterpret_cast<const unsigned*>(tb + tMh)[p];
+      const float g2p = sG2[p];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const float4 g2 = *reinterpret_cast<const float4*>(sG2 + 16 * mb + 4 * g4);
+        const float gj[4] = {g2.x, g2.y, g2.z, g2.w};
+        const unsigned mword = mb >= 2 ? mhi : mlo;
+        f32x4 wv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * mb + 4 * g4 + r;
+          const bool anc = mode ? ((mword >> (j & 31)) & 1u) : (j <= p);
+          wv[r] = anc ? Vt[mb][r] * __builtin_amdgcn_exp2f(g2p - gj[r]) : 0.f;
+        }
+        Wb[mb] = to_bf4(wv);
+      }
+    }
+    const float cS = sEG[p];
+    const bf16x8 w01 = cat8b(Wb[0], Wb[1]), w23 = cat8b(Wb[2], Wb[3]);
+    f32x4 acc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      // A operand: K^T rows (d_k) of this state block against tokens 0..31 and 32..63
+      const unsigned char* kp = kq + o.KT[dt];
+      const bf16x8 k01 = cat8(tr_read(kp), tr_read(kp + 4096));
+      const bf16x8 k23 = cat8(tr_read(kp + 8192), tr_read(kp + 8192 + 4096));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[dt][r] = cS * ST[dt][r];
+      acc[dt] = mma32(k01, w01, acc[dt]);
+      acc[dt] = mma32(k23, w23, acc[dt]);
+    }
+    const int fs = reinterpret_cast<const int*>(tb + tFS)[p];
+    const int sr = reinterpret_cast<const int*>(tb + tSR)[p];
+    const size_t roff = (size_t)(v0w + l16) * DK + 8 * g4;
+    if (fs >= 0) {
+      float* dst = a.fork_states + ((size_t)fs * a.H + h) * SS + roff;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4*>(dst + 32 * (dt >> 1) + 4 * (dt & 1)) = acc[dt];
+    }
+    if (sr >= 0) {
+      float* dst = a.state_out + ((size_t)sr * a.H + h) * SS + roff;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4*>(dst + 32 * (dt >> 1) + 4 * (dt & 1)) = acc[dt];
+    }
+    if (need_exit && p == n - 1) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) ST[dt] = acc[dt];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Sb[m] = cat8b(to_bf4(ST[2 * m]), to_bf4(ST[2 * m + 1]));
+    }
+  } while (todo);
+}
+
+template <int BV>
+__device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, int ws, int lane) {
+  using C = Cfg<BV>;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  SOff o;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) o.F[m] = l16 * 256 + (((4 * m + g4) ^ kq_swz(l16)) << 4);
+  // lane i of a 16-lane group receives d_k column 32 m + 8 (i / 4) + 4 bb + i % 4 of
+  // rows 4 g4 .. 4 g4 + 3 (dt = 2 m + bb)
+  {
+    const int r0 = 4 * g4 + (l16 >> 2), p = l16 & 3;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o.KT[dt] = r0 * 256 + ((((4 * (dt >> 1) + p) ^ kq_swz(r0))) << 4) + ((dt & 1) << 3);
+  }
+  {
+    const int vrow = 4 * g4 + (l16 >> 2), vcol = 16 * ws + (l16 & 3) * 4;
+    o.V = vrow * BV * 2 + (((vcol >> 3) ^ v_swz<BV>(vrow)) << 4) + ((vcol & 7) << 1);
+  }
+  f32x4 ST[8];
+  bf16x8 Sb[4];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) ST[dt] = zero;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) Sb[m] = cat8b(to_bf4(zero), to_bf4(zero));
+
+  lds_barrier();  // the helpers' iteration -1
+  for (int it = 0;; ++it) {
+    const unsigned char* tb = smem + C::oTB + (it % 3) * kTB;
+    const Desc* dp = reinterpret_cast<const Desc*>(tb + tD);
+    if (!rfl(dp->valid)) break;
+    const int t0 = rfl(dp->t0), n = rfl(dp->n), h = rfl(dp->h), v0 = rfl(dp->v0);
+    const int mode = rfl(dp->mode);
+    const bool has_out = rfl(dp->has_out), need_exit = rfl(dp->need_exit), first = rfl(dp->first);
+    unsigned long long todo = ((unsigned long long)(unsigned)rfl((int)dp->req_hi) << 32) | (unsigned)rfl((int)dp->req_lo);
+    if (need_exit) todo |= 1ull << (n - 1);
+    const unsigned char* kq = smem + C::oKQ + (it % 3) * 32768;
+    const unsigned char* vt = smem + C::oV + (it & 1) * C::VT;
+    const unsigned char* pr = smem + C::oPR + (it & 1) * kPR;
+    const int v0w = v0 + 16 * ws;  // first column of the wave
+
+    if (first) {
+      const unsigned long long sp = (unsigned long long)dp->sin;
+      const float* sin = (const float*)(((unsigned long long)(unsigned)rfl((int)(sp >> 32)) << 32) | (unsigned)rfl((int)sp));
+      if (sin) {
+        const float* row = sin + (size_t)(16 * ws + l16) * DK + 8 * g4;
+        f32x4 t[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          t[dt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 32 * (dt >> 1) + 4 * (dt & 1)));
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) ST[dt] = t[dt];
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) ST[dt] = zero;
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Sb[m] = cat8b(to_bf4(ST[2 * m]), to_bf4(ST[2 * m + 1]));
+    }
+    if (has_out) state_chunk<BV, true>(a, tb, kq, vt, pr, o, ST, Sb, t0, n, h, v0w, mode, need_exit, todo, lane);
+    else state_chunk<BV, false>(a, tb, kq, vt, pr, o, ST, Sb, t0, n, h, v0w, mode, need_exit, todo, lane);
+    lds_barrier();
+  }
+}
+
+// ------------------------------------------------------------------ kernel
+
+template <int BV>
+__global__ void __launch_bounds__(Cfg<BV>::NTHR, 1) k_walk_pipe(const Args a) {
+  using C = Cfg<BV>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = rfl(tid >> 6);  // wave index (uniform)
+  if (*a.err != kNoError) return;  // structural error: nothing is computed
+  const int count = a.level_count[a.level];
+  const int base = a.level_ptr[a.level];
+  const int xcd = blockIdx.x % kXcd;
+  const int per_xcd = gridDim.x / kXcd;
+  const bool helper = w >= C::NS;
+  const int hid = w - C::NS;  // 0 or 1 on the helpers
+
+  // Pairs of P whose second 16-token block lies above the diagonal ((0, 1) and
+  // (2, 3)) are never written: clear them once in both product buffers.
+  for (int e = tid; e < 2 * 2 * 64; e += C::NTHR) {
+    const int slot = e >> 7, which = (e >> 6) & 1, ln = e & 63;
+    *reinterpret_cast<uint2*>(smem + C::oPR + slot * kPR + pP + (which ? 3 : 0) * 1024 + ln * 16 + 8) = make_uint2(0, 0);
+  }
+
+  // ---- prologue: describe chunks 0 and 1 and copy K, Q and the token tables
+  // of chunk 0; the helpers' first loop iteration forms its products
+  Desc* nds = reinterpret_cast<Desc*>(smem + C::oND);
+  Feed f;
+  f.cur = false;
+  f.li = blockIdx.x / kXcd;
+  f.nx_valid = false;
+  if (hid == 1) {
+    feed_prefetch(f, a, xcd, count, base);
+    wait_vm();
+    put_desc(reinterpret_cast<unsigned char*>(nds + 0), feed_next<BV>(f, a, xcd, count, base, per_xcd), lane);
+    wait_vm();
+    put_desc(reinterpret_cast<unsigned char*>(nds + 1), feed_next<BV>(f, a, xcd, count, base, per_xcd), lane);
+  }
+  lds_barrier();
+  if (helper) {
+    const Desc d0 = uniform_desc(nds[0]);
+    TokenRegs tr;
+    if (hid == 1) tr = load_tokens(a, d0, lane);
+    if (d0.valid) issue_kq(a, d0, smem + C::oKQ, hid, lane);
+    wait_vm();
+    if (hid == 1) store_tokens(a, d0, tr, smem + C::oTB, lane);
+  }
+  lds_barrier();
+
+  if (helper) helper_loop<BV>(a, smem, hid, lane, f, xcd, count, base, per_xcd);
+  else state_loop<BV>(a, smem, w, lane);
+}
+
+template <int BV>
+hipError_t run(const Args& wa, int levels, hipStream_t s) {
+  auto kern = k_walk_pipe<BV>;
+  constexpr int bytes = Cfg<BV>::bytes;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     bytes);
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // one workgroup per CU (bounded by LDS), persistent over the level's items;
+  // a multiple of the XCD count so that every XCD has the same number of workgroups
+  const int grid = cus >= kXcd ? cus / kXcd * kXcd : kXcd;
+  for (int l = 0; l < levels; ++l) {
+    Args x = wa;
+    x.level = l;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(Cfg<BV>::NTHR), bytes, s, x);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool walk_pipe_supported(int dtype, int dk, int bv) {
+  return dtype == GDN_BF16 && dk == DK && (bv == 16 || bv == 32 || bv == 64);
+}
+
+bool walk_pipe_fits(const gdn_tree_dims& d) {
+  // the kernel addresses q, k, v, out and pseudo_v with 32-bit element offsets
+  const long long per_token = (long long)d.H * (d.Dk > d.Dv ? d.Dk : d.Dv);
+  return d.T * per_token < (1ll << 30);
+}
+
+hipError_t launch_walk_pipe(const gdn_tree_fwd_args& fa, const Meta& m, int bv, hipStream_t s) {
+  Args wa;
+  wa.q = reinterpret_cast<const __bf16*>(fa.q);
+  wa.k = reinterpret_cast<const __bf16*>(fa.k);
+  wa.v = reinterpret_cast<const __bf16*>(fa.v);
+  wa.g = reinterpret_cast<const __bf16*>(fa.log_gate);
+  wa.b = reinterpret_cast<const __bf16*>(fa.beta);
+  wa.parent = fa.parent_idx;
+  wa.init = fa.init_state;
+  wa.out = reinterpret_cast<__bf16*>(fa.out);
+  wa.state_out = fa.state_out;
+  wa.pv = fa.pseudo_v;
+  wa.fork_states = m.fork_states;
+  wa.unit_info = m.unit_info;
+  wa.out_map = m.out_map;
+  wa.state_map = m.state_map;
+  wa.fork_slot = m.fork_slot;
+  wa.tree_mask = m.tree_mask;
+  wa.err = m.err;
+  wa.level_count = m.level_count;
+  wa.level_ptr = m.level_ptr;
+  wa.H = fa.dims.H;
+  wa.Dv = fa.dims.Dv;
+  wa.NT = fa.dims.Dv / bv;
+  wa.level = 0;
+  wa.out_all = fa.out_rows == nullptr;
+  const int L = fa.dims.max_levels;
+  switch (bv) {
+    case 16: return run<16>(wa, L, s);
+    case 32: return run<32>(wa, L, s);
+    case 64: return run<64>(wa, L, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gdn
