@@ -141,6 +141,8 @@ typedef struct gdn_tree_dims {
  *  dv_tile                   columns of Dv one workgroup carries: 0 = automatic, else 16, 32
  *                            or 64 dividing Dv. Results are bitwise the same for every choice.
  *  flags                     0 or GDN_FWD_PLANNED
+ * Alignment: q, k, v, out, init_state, state_out and pseudo_v must be 16-byte
+ * aligned (GDN_ERR_ARGS otherwise); the kernels move them in 8- and 16-byte pieces.
  */
 typedef struct gdn_tree_fwd_args {
   gdn_tree_dims dims;

@@ -87,6 +87,12 @@ def test_forward_argument_errors_need_no_gpu():
     a.q = ctypes.c_void_p(8194)
     assert B.lib.gdn_tree_forward(ctypes.byref(a), None) == -6  # misaligned
     assert b"aligned" in B.lib.gdn_tree_last_error()
+    a.q = ctypes.c_void_p(8192)
+    for f in ["out", "init_state", "pseudo_v"]:  # moved in 8- and 16-byte pieces
+        setattr(a, f, ctypes.c_void_p(8200))
+        assert B.lib.gdn_tree_forward(ctypes.byref(a), None) == -6, f
+        assert b"aligned" in B.lib.gdn_tree_last_error()
+        setattr(a, f, ctypes.c_void_p(8192) if f == "out" else None)
 
 
 def test_capacities_match_reference_planner():

@@ -70,7 +70,9 @@ int check_fwd(const gdn_tree_fwd_args* a, bool walk, LayoutFull* L) {
   if (a->flags & ~GDN_FWD_PLANNED) return fail(GDN_ERR_ARGS, "unknown flags");
   if (!walk) return GDN_OK;
   if (!a->q || !a->k || !a->v || !a->log_gate || !a->beta) return fail(GDN_ERR_NULL, "q, k, v, log_gate and beta are required");
-  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v)) return fail(GDN_ERR_ARGS, "q, k, v must be 16-byte aligned");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out) || !aligned16(a->init_state) ||
+      !aligned16(a->state_out) || !aligned16(a->pseudo_v))
+    return fail(GDN_ERR_ARGS, "q, k, v, out, init_state, state_out and pseudo_v must be 16-byte aligned");
   if (!a->out_rows && a->n_out != d.T) return fail(GDN_ERR_ARGS, "without out_rows, n_out must be T");
   if ((a->n_out > 0 || (!a->out_rows && d.T > 0)) && !a->out) return fail(GDN_ERR_NULL, "out is NULL");
   if (a->n_state > 0 && !a->state_out) return fail(GDN_ERR_NULL, "state_out is NULL");

@@ -20,7 +20,8 @@
 // one (segment, head, d_v tile) item after another and splits each chunk's
 // work by that line:
 //
-// * state waves (one per 16 columns of the d_v tile) hold their rows of S in
+// * state waves (one per 16 columns of the d_v tile, per 32 in a tile of 64)
+//   hold their rows of S in
 //   fp32 registers and do everything that involves S: K S_e^T, R, the block
 //   substitution, Q S_e^T and P Vt, the outputs and pseudo-values, and the
 //   states after requested tokens and at the chunk exit;
@@ -71,15 +72,18 @@ constexpr int kTB = 2368;
 constexpr int pNA = 0;              // 6 blocks x 64 lanes x 8 B: -A_bm (m < b), 16x16x16 A operands
 constexpr int kDIS = 640;           // stride between diagonal inverses (512 B used)
 constexpr int pDI = 3072;           // 4 blocks: (I + A_bb)^{-1}, 16x16x16 A operands
-constexpr int pP = pDI + 4 * kDIS;  // 6 pairs x 64 lanes x 16 B: P row block x 32 tokens, 16x16x32 A operands
-constexpr int kPR = pP + 6 * 1024;
+constexpr int kPR = pDI + 4 * kDIS;
+// P of one chunk: 6 pairs x 64 lanes x 16 B (row block x 32 tokens), 16x16x32 operands.
+// It lives one iteration longer than the other products: the state waves
+// finish a chunk's output during the next chunk.
+constexpr int kPP = 6 * 1024;
 // fp32 staging of one helper's diagonal blocks of A, transposed: [4][16][kLTR] + pad
 constexpr int kLTR = 20;
 constexpr int kLTS = 16 * kLTR + 4;
 
 template <int BV>
 struct Cfg {
-  static constexpr int NB = 1;                 // 16-column blocks per state wave
+  static constexpr int NB = BV == 64 ? 2 : 1;  // 16-column blocks per state wave
   static constexpr int NS = BV / (16 * NB);    // state waves
   static constexpr int NW = NS + 2;            // plus two helpers
   static constexpr int NTHR = 64 * NW;
@@ -89,12 +93,14 @@ struct Cfg {
   static constexpr int oKQ = 0;                  // [3] K tile (16 KB) then Q tile (16 KB)
   static constexpr int oTB = oKQ + 3 * 32768;    // [3] token tables
   static constexpr int oV = oTB + 3 * kTB;       // [2] V tiles bf16 [64][BV]
-  static constexpr int oPR = oV + 2 * VT;        // [2] products
-  static constexpr int oLT = oPR + 2 * kPR;      // diagonal-block staging
+  static constexpr int oPR = oV + 2 * VT;        // [2] -A blocks and diagonal inverses
+  static constexpr int oPP = oPR + 2 * kPR;      // [3] P
+  static constexpr int oLT = oPP + 3 * kPP;      // diagonal-block staging
   static constexpr int oND = oLT + 4 * kLTS * 4; // [2] descriptors of chunks to copy, by parity
   static constexpr int bytes = oND + 128;
   static_assert(bytes <= 160 * 1024, "LDS budget");
-  static_assert(oTB % 16 == 0 && oV % 16 == 0 && oPR % 16 == 0 && oLT % 16 == 0 && oND % 16 == 0, "alignment");
+  static_assert(oTB % 16 == 0 && oV % 16 == 0 && oPR % 16 == 0 && oPP % 16 == 0 && oLT % 16 == 0 && oND % 16 == 0,
+                "alignment");
 };
 
 struct Desc {
@@ -140,15 +146,19 @@ __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // 16 bytes per lane from global memory (sbase + voff) straight into LDS: lane
-// i's bytes land at lds_base + 16 i. Issued as inline assembly so that the
+// i's bytes land at lds_addr + 16 i. Issued as inline assembly so that the
 // compiler does not treat the copy as a pending write to all of LDS (it would
 // otherwise wait for it before every LDS access); completion is awaited
 // explicitly with wait_vm(). M0 holds the LDS base for the instruction; nothing
 // else in this kernel uses M0.
-__device__ __forceinline__ void dma16(const void* sbase, unsigned voff, const void* lds_base) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((const lds_void*)lds_base));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(l), "v"(voff), "s"(sbase)
+__device__ __forceinline__ void dma16(const void* sbase, unsigned voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
                : "memory");
+}
+
+// LDS address of a byte of the kernel's shared buffer (32-bit, wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr_of(const unsigned char* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((const lds_void*)p));
 }
 
 // 16-byte piece p of row r of a K or Q tile sits at slot p ^ kq_swz(r).
@@ -216,8 +226,7 @@ __device__ __forceinline__ void feed_prefetch(Feed& f, const Args& a, int xcd, i
 // Reads the prefetched unit record: call it only after a vmcnt(0).
 template <int BV>
 __device__ __forceinline__ Desc feed_next(Feed& f, const Args& a, int xcd, int count, int base, int per_xcd) {
-  Desc d;
-  d.valid = 0;
+  Desc d = {};  // every field defined, also when the level is done
   if (!(f.cur && f.c < f.nch)) {
     f.cur = false;
     if (!f.nx_valid) return d;
@@ -284,46 +293,65 @@ __device__ __forceinline__ void put_desc(unsigned char* p, const Desc& d, int la
 
 // ------------------------------------------------------------ chunk loads
 
-// Helper hid's share of the direct-to-LDS copies of the K and Q rows of chunk
-// d into slot kq (K at +0, Q at +16384). Rows at or beyond d.n are zero-filled.
-__device__ __forceinline__ void issue_kq(const Args& a, const Desc& d, unsigned char* kq, int hid, int lane) {
+// Direct-to-LDS copies of 4-row blocks [b0, b1) of the K (or Q) rows of
+// chunk d into the tile at tile (LDS). Lane (g4, l16) copies row
+// 4 blk + g4, 16-byte piece l16 ^ kq_swz(row), into slot l16 of that row. Rows
+// at or beyond d.n are zero-filled. The global address advances from the
+// block's first row, so no per-block pointer outlives an iteration.
+template <int B0, int B1>
+__device__ __forceinline__ void issue_rows(const Args& a, const Desc& d, const __bf16* x, unsigned char* tile, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
-  const bool full = d.n == kChunk;
-  // row 4 blk + g4, slot l16 holds piece l16 ^ kq_swz(row)
-  const unsigned row0 = (((unsigned)d.t0 + g4) * (unsigned)a.H + d.h) * (DK * 2);
-  const unsigned step = 4u * a.H * (DK * 2);  // bytes per instruction (4 rows)
+  const unsigned rs = (unsigned)a.H * (DK * 2);  // bytes per token row
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(x) + ((size_t)d.t0 * a.H + d.h) * (DK * 2) +
+                             (size_t)(4 * B0) * rs;
+  unsigned vo[4];  // the piece permutation depends on blk & 3
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int ins = 2 * j + hid;
-    const bool isK = ins < 16;
-    const int blk = ins & 15;
-    const int row = 4 * blk + g4;
-    unsigned char* dst = kq + (isK ? 0 : 16384) + blk * 1024;
-    const unsigned char* sbase = reinterpret_cast<const unsigned char*>(isK ? a.k : a.q) + (size_t)blk * step;
-    const unsigned voff = row0 + (unsigned)((l16 ^ ((g4 << 2) | (blk & 3))) * 16);
-    if (full || row < d.n) dma16(sbase, voff, dst);
-    else *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
+  for (int k = 0; k < 4; ++k) vo[k] = g4 * rs + (unsigned)((l16 ^ ((g4 << 2) | k)) << 4);
+  const size_t step = (size_t)4 * rs;
+  if (d.n == kChunk) {
+    const uint32_t l0 = lds_addr_of(tile);
+#pragma unroll
+    for (int blk = B0; blk < B1; ++blk) {
+      dma16(src, vo[blk & 3], l0 + blk * 1024);
+      src += step;
+    }
+  } else {
+#pragma unroll
+    for (int blk = B0; blk < B1; ++blk) {
+      if (4 * blk + g4 < d.n) dma16(src, vo[blk & 3], lds_addr_of(tile + blk * 1024));
+      else *reinterpret_cast<uint4*>(tile + blk * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+      src += step;
+    }
   }
 }
 
-// Helper hid's share of the copies of the V tile of chunk d into vb.
+// The V tile of chunk d into vb: pieces of RPI rows each; lane takes row
+// ins * RPI + lane / VPR, slot lane % VPR.
 template <int BV>
-__device__ __forceinline__ void issue_v(const Args& a, const Desc& d, unsigned char* vb, int hid, int lane) {
+__device__ __forceinline__ void issue_v(const Args& a, const Desc& d, unsigned char* vb, int lane) {
   using C = Cfg<BV>;
-  const bool full = d.n == kChunk;
-  // row ins * RPI + lane / VPR, slot lane % VPR
   const int vr = lane / C::VPR, vs = lane % C::VPR;
-  const unsigned row0 = (((unsigned)d.t0 + vr) * (unsigned)a.H + d.h) * (unsigned)(a.Dv * 2) + (unsigned)d.v0 * 2 +
-                        (unsigned)((vs ^ v_swz<BV>(vr)) * 16);
-  const unsigned step = (unsigned)C::RPI * a.H * (a.Dv * 2);
+  const unsigned rs = (unsigned)a.H * (unsigned)(a.Dv * 2);
+  const unsigned vo = vr * rs + (unsigned)((vs ^ v_swz<BV>(vr)) * 16);
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(a.v) + ((size_t)d.t0 * a.H + d.h) * (size_t)(a.Dv * 2) +
+                             (size_t)d.v0 * 2;
+  const size_t step = (size_t)C::RPI * rs;
 #pragma unroll
   for (int ins = 0; ins < C::VPR; ++ins) {
-    if ((ins & 1) != hid) continue;
     const int row = ins * C::RPI + vr;
-    unsigned char* dst = vb + ins * 1024;
-    const unsigned char* sbase = reinterpret_cast<const unsigned char*>(a.v) + (size_t)ins * step;
-    if (full || row < d.n) dma16(sbase, row0, dst);
-    else *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0, 0, 0, 0);
+    if (d.n == kChunk || row < d.n) dma16(src, vo, lds_addr_of(vb + ins * 1024));
+    else *reinterpret_cast<uint4*>(vb + ins * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+    src += step;
+  }
+}
+
+// Helper 0 copies K and the first half of Q, helper 1 the rest of Q.
+__device__ __forceinline__ void issue_kq(const Args& a, const Desc& d, unsigned char* kq, int hid, int lane) {
+  if (hid == 0) {
+    issue_rows<0, 16>(a, d, a.k, kq, lane);
+    issue_rows<0, 8>(a, d, a.q, kq + 16384, lane);
+  } else {
+    issue_rows<8, 16>(a, d, a.q, kq + 16384, lane);
   }
 }
 
@@ -354,6 +382,22 @@ __device__ __forceinline__ TokenRegs load_tokens(const Args& a, const Desc& d, i
   return r;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within rows of 16
+// lanes, then the last lane of a row added to the rows after it.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x = dpp_add<0x111, 0xf>(x);  // row_shr:1
+  x = dpp_add<0x112, 0xf>(x);  // row_shr:2
+  x = dpp_add<0x114, 0xf>(x);  // row_shr:4
+  x = dpp_add<0x118, 0xf>(x);  // row_shr:8
+  x = dpp_add<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // Token tables of chunk d into tb (second helper).
 __device__ __forceinline__ void store_tokens(const Args& a, Desc d, const TokenRegs& r, unsigned char* tb, int lane) {
   if (!d.valid) {
@@ -380,15 +424,11 @@ __device__ __forceinline__ void store_tokens(const Args& a, Desc d, const TokenR
     }
     mask = a.tree_mask[(size_t)d.sq * kChunk + i];
   } else {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(G, off);
-      if (i >= off) G += o;
-    }
+    G = wave_prefix_sum(G);
     mask = (i == 63) ? ~0ull : ((2ull << i) - 1ull);
   }
   const float g2 = G * kLog2e;
-  const float g2last = __shfl(g2, d.n - 1);
+  const float g2last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g2), d.n - 1));
   const int orow = (valid && r.om != kUnmapped) ? r.om : -1;
   const int fs = valid ? r.fs : -1;
   const int sr = (valid && r.sm != kUnmapped) ? r.sm : -1;
@@ -410,47 +450,48 @@ __device__ __forceinline__ void store_tokens(const Args& a, Desc d, const TokenR
 
 // ---------------------------------------------------------------- helpers
 
-// The S-independent operands of one chunk. Helper 0 takes the tiles of token
-// row blocks 0..2, helper 1 those of row block 3; each inverts its own
-// diagonal blocks. The Gram and Q K^T tiles are computed with K of the column
-// block as the A operand, so that the accumulator of tile (row block b,
-// column block m) holds row 16 b + l16, columns 16 m + 4 g4 .. + 3: exactly the
-// A-operand layout the state waves read.
-template <int HID, bool HAS_OUT>
-__device__ __forceinline__ void products(const unsigned char* kq, const unsigned char* tb, unsigned char* pr, float* lt,
-                                         bool tree, int lane) {
-  constexpr int R0 = HID == 0 ? 0 : 3, R1 = HID == 0 ? 3 : 4;  // token row blocks [R0, R1)
+// The S-independent operands of one chunk. The Gram and Q K^T tiles are
+// computed with K of the column block as the A operand, so that the
+// accumulator of tile (row block b, column block m) holds row 16 b + l16,
+// columns 16 m + 4 g4 .. + 3: exactly the A-operand layout the state waves
+// read. Helper 0 (DIAG) takes the four diagonal tiles and inverts the
+// diagonal blocks of I + A; helper 1 takes the six tiles below them.
+template <bool DIAG, bool HAS_OUT>
+__device__ __forceinline__ void products(const unsigned char* kq, const unsigned char* tb, unsigned char* pr,
+                                         unsigned char* pp, float* lt, bool tree, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
   int oF[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) oF[ks] = l16 * 256 + (((4 * ks + g4) ^ kq_swz(l16)) << 4);
-  bf16x8 KF[4][4];
+  bf16x8 KF[4][4], QF[4][4];
 #pragma unroll
-  for (int b = 0; b < R1; ++b)
+  for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) KF[b][ks] = lds_at<bf16x8>(kq + oF[ks], b * 4096);
+  if (HAS_OUT) {
+#pragma unroll
+    for (int rb = DIAG ? 0 : 1; rb < 4; ++rb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) QF[rb][ks] = lds_at<bf16x8>(kq + 16384 + oF[ks], rb * 4096);
+  }
   const float* G2 = reinterpret_cast<const float*>(tb + tG2);
   const float* Bt = reinterpret_cast<const float*>(tb + tB);
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int rb = R0; rb < R1; ++rb) {
-    bf16x8 QF[4];
-    if (HAS_OUT) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) QF[ks] = lds_at<bf16x8>(kq + 16384 + oF[ks], rb * 4096);
-    }
+  for (int rb = DIAG ? 0 : 1; rb < 4; ++rb) {
     const int i = 16 * rb + l16;
     const float g2i = G2[i], bi = Bt[i];
     const unsigned mw0 = reinterpret_cast<const unsigned*>(tb + tMl)[i];
     const unsigned mw1 = reinterpret_cast<const unsigned*>(tb + tMh)[i];
 #pragma unroll
     for (int cb = 0; cb <= rb; ++cb) {
+      if (DIAG != (cb == rb)) continue;
       f32x4 ga = zero, gp = zero;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) ga = mma32(KF[cb][ks], KF[rb][ks], ga);
       if (HAS_OUT) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) gp = mma32(KF[cb][ks], QF[ks], gp);
+        for (int ks = 0; ks < 4; ++ks) gp = mma32(KF[cb][ks], QF[rb][ks], gp);
       }
       const float4 gj4 = *reinterpret_cast<const float4*>(G2 + 16 * cb + 4 * g4);
       const float gj[4] = {gj4.x, gj4.y, gj4.z, gj4.w};
@@ -463,7 +504,7 @@ __device__ __forceinline__ void products(const unsigned char* kq, const unsigned
         const bool anc = tree ? in_tree : (cb < rb || jl <= l16);
         e[r] = anc ? __builtin_amdgcn_exp2f(g2i - gj[r]) : 0.f;
       }
-      if (cb < rb) {
+      if (!DIAG) {
         bf16x4 na;
 #pragma unroll
         for (int r = 0; r < 4; ++r) na[r] = (__bf16)(-(bi * e[r] * ga[r]));
@@ -479,43 +520,55 @@ __device__ __forceinline__ void products(const unsigned char* kq, const unsigned
 #pragma unroll
         for (int r = 0; r < 4; ++r) pv[r] = (__bf16)(e[r] * gp[r]);
         const int pair = (rb <= 1 ? rb : 2 * rb - 2) + (cb >> 1);
-        *reinterpret_cast<bf16x4*>(pr + pP + pair * 1024 + lane * 16 + (cb & 1) * 8) = pv;
+        *reinterpret_cast<bf16x4*>(pp + pair * 1024 + lane * 16 + (cb & 1) * 8) = pv;
       }
     }
   }
+  if (!DIAG) return;
   wait_lds();
   // Row c = l16 of (I + L)^{-1} for the diagonal block g4, by back substitution
-  // on the transposed system (I + L)^T z = e_c, in fp32.
-  if (g4 >= R0 && g4 < R1) {
-    const float* L = lt + g4 * kLTS;  // L[r * kLTR + c'] = A[c'][r] of the block
-    float z[16];
+  // on the transposed system (I + L)^T z = e_c, in fp32. The block's entries are
+  // read first; each sum runs from the far end so that only its last term waits
+  // for the entry just solved.
+  const float* L = lt + g4 * kLTS;  // L[r * kLTR + c'] = A[c'][r] of the block
+  float Lr[16][16];
 #pragma unroll
-    for (int r = 15; r >= 0; --r) {
-      float acc = (r == l16) ? 1.f : 0.f;
+  for (int r = 0; r < 15; ++r)
 #pragma unroll
-      for (int c = r + 1; c < 16; ++c) acc -= L[r * kLTR + c] * z[c];
-      z[r] = acc;
+    for (int q = (r + 1) / 4; q < 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(L + r * kLTR + 4 * q);
+      Lr[r][4 * q] = v.x;
+      Lr[r][4 * q + 1] = v.y;
+      Lr[r][4 * q + 2] = v.z;
+      Lr[r][4 * q + 3] = v.w;
     }
-    unsigned char* d = pr + pDI + g4 * kDIS;
+  float z[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bf16x4 v;
+  for (int r = 15; r >= 0; --r) {
+    float acc = (r == l16) ? 1.f : 0.f;
 #pragma unroll
-      for (int y = 0; y < 4; ++y) v[y] = (__bf16)z[4 * q + y];
-      *reinterpret_cast<bf16x4*>(d + (q * 16 + l16) * 8) = v;
-    }
+    for (int c = 15; c > r; --c) acc -= Lr[r][c] * z[c];
+    z[r] = acc;
+  }
+  unsigned char* d = pr + pDI + g4 * kDIS;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    bf16x4 v;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) v[y] = (__bf16)z[4 * q + y];
+    *reinterpret_cast<bf16x4*>(d + (q * 16 + l16) * 8) = v;
   }
 }
 
 __device__ __forceinline__ void chunk_products(int hid, const Desc& c, const unsigned char* kq, const unsigned char* tb,
-                                      unsigned char* pr, float* lt, int lane) {
+                                               unsigned char* pr, unsigned char* pp, float* lt, int lane) {
   const bool tree = c.mode != 0;
   if (hid == 0) {
-    if (c.has_out) products<0, true>(kq, tb, pr, lt, tree, lane);
-    else products<0, false>(kq, tb, pr, lt, tree, lane);
+    if (c.has_out) products<true, true>(kq, tb, pr, pp, lt, tree, lane);
+    else products<true, false>(kq, tb, pr, pp, lt, tree, lane);
   } else {
-    if (c.has_out) products<1, true>(kq, tb, pr, lt, tree, lane);
-    else products<1, false>(kq, tb, pr, lt, tree, lane);
+    if (c.has_out) products<false, true>(kq, tb, pr, pp, lt, tree, lane);
+    else products<false, false>(kq, tb, pr, pp, lt, tree, lane);
   }
 }
 
@@ -531,19 +584,20 @@ __device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, 
     if (it >= 0 && !rfl(reinterpret_cast<const Desc*>(smem + C::oTB + (it % 3) * kTB + tD)->valid)) break;
     const int s1 = (it + 1) % 3, s2 = (it + 2) % 3;
     unsigned char* tb1 = smem + C::oTB + s1 * kTB;
-    const Desc nd = uniform_desc(nds[it & 1]);                              // chunk it + 2: copy K, Q
-    const Desc nx = uniform_desc(*reinterpret_cast<const Desc*>(tb1 + tD));  // chunk it + 1: copy V, products
+    const Desc nd = uniform_desc(nds[it & 1]);                              // chunk it + 2: K, Q, tables
+    const Desc nx = uniform_desc(*reinterpret_cast<const Desc*>(tb1 + tD));  // chunk it + 1: V, products
     if (hid == 1) tr = load_tokens(a, nd, lane);
     if (nd.valid) issue_kq(a, nd, smem + C::oKQ + s2 * 32768, hid, lane);
-    if (nx.valid) issue_v<BV>(a, nx, smem + C::oV + ((it + 1) & 1) * C::VT, hid, lane);
-    if (nx.valid) chunk_products(hid, nx, smem + C::oKQ + s1 * 32768, tb1, smem + C::oPR + ((it + 1) & 1) * kPR, lt, lane);
+    if (hid == 1 && nx.valid) issue_v<BV>(a, nx, smem + C::oV + ((it + 1) & 1) * C::VT, lane);
+    if (nx.valid)
+      chunk_products(hid, nx, smem + C::oKQ + s1 * 32768, tb1, smem + C::oPR + ((it + 1) & 1) * kPR,
+                     smem + C::oPP + s1 * kPP, lt, lane);
     wait_vm();  // this wave's copies, token values and unit record have landed
     if (hid == 1) {
-      Desc nn;
-      nn.valid = 0;
+      store_tokens(a, nd, tr, smem + C::oTB + s2 * kTB, lane);
+      Desc nn = {};
       if (nd.valid) nn = feed_next<BV>(f, a, xcd, count, base, per_xcd);
       put_desc(reinterpret_cast<unsigned char*>(nds + ((it + 1) & 1)), nn, lane);
-      store_tokens(a, nd, tr, smem + C::oTB + s2 * kTB, lane);
     }
     lds_barrier();
   }
@@ -552,66 +606,77 @@ __device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, 
 // ------------------------------------------------------------ state waves
 
 // Per-lane LDS offsets of a state wave.
+template <int NB>
 struct SOff {
-  int F[4];   // row fragment of K or Q rows 0..15, 16 B per lane (row block rb adds 4096 rb)
-  int KT[8];  // transposed read of K rows 4 g4 + l16/4 for state block dt (rows + 16 add 4096)
-  int V;      // transposed read of V rows 4 g4 + l16/4, the wave's 16 columns (row block rb adds 32 BV rb)
+  int F[4];    // row fragment of K or Q rows 0..15, 16 B per lane (row block rb adds 4096 rb)
+  int KT[8];   // transposed read of K rows 4 g4 + l16/4 for state block dt (rows + 16 add 4096)
+  int V[NB];   // transposed read of V rows 4 g4 + l16/4, column block nb (row block rb adds 32 BV rb)
 };
 
 // One chunk on a state wave: K S_e^T, R, the block substitution, the outputs
 // and pseudo-values, then the states after requested tokens and at the exit.
-// ST[dt] (dt = 2 m + bb) holds S^T of the wave's columns in the accumulator
-// layout, lane (l16, g4) holding S[col][32 m + 8 g4 + 4 bb + r]; Sb[m] is its
-// bf16 B operand for d_k 32 m .. 32 m + 31 in natural k order.
+// The wave owns NB blocks of 16 columns. ST[nb][dt] (dt = 2 m + bb) holds S^T
+// of block nb in the accumulator layout, lane (l16, g4) holding
+// S[col][32 m + 8 g4 + 4 bb + r]; Sb[nb][m] is its bf16 B operand (and, as the
+// same registers, the A operand of S_e Q^T) for d_k 32 m .. 32 m + 31.
 template <int BV, bool HAS_OUT>
-__device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* tb, const unsigned char* kq,
-                                            const unsigned char* vt, const unsigned char* pr, const SOff& o,
-                                            f32x4 (&ST)[8], bf16x8 (&Sb)[4], int t0, int n, int h, int v0w, int mode,
+__device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* smem, const unsigned char* tb,
+                                            const unsigned char* kq, const unsigned char* vt, const unsigned char* pr,
+                                            const SOff<Cfg<BV>::NB>& o, f32x4 (&ST)[Cfg<BV>::NB][8],
+                                            bf16x8 (&Sb)[Cfg<BV>::NB][4], int it, int t0, int n, int h, int v0w, int mode,
                                             bool need_exit, unsigned long long todo, int lane) {
+  constexpr int NB = Cfg<BV>::NB;
   const int g4 = lane >> 4, l16 = lane & 15;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const unsigned HDv = (unsigned)a.H * a.Dv;
-  const unsigned hcol = (unsigned)h * a.Dv + (unsigned)(v0w + l16);  // column within a token row of out / pv
   const float* sEG = reinterpret_cast<const float*>(tb + tEG);
   const float* sB = reinterpret_cast<const float*>(tb + tB);
 
-  // K S_e^T and Q S_e^T for the wave's columns
-  f32x4 X[4], O[4];
+  // K S_e^T for the wave's columns
+  f32x4 X[NB][4];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     bf16x8 KF[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) KF[m] = lds_at<bf16x8>(kq + o.F[m], rb * 4096);
-    X[rb] = zero;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) X[rb] = mma32(KF[m], Sb[m], X[rb]);
+    for (int nb = 0; nb < NB; ++nb) {
+      X[nb][rb] = zero;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) X[nb][rb] = mma32(KF[m], Sb[nb][m], X[nb][rb]);
+    }
   }
+  // e^G S_e Q^T (the output, transposed): lane holds four columns of one token
+  f32x4 O[NB][4];
   if (HAS_OUT) {
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       bf16x8 QF[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) QF[m] = lds_at<bf16x8>(kq + 16384 + o.F[m], rb * 4096);
-      O[rb] = zero;
+      const float egt = sEG[16 * rb + l16];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) O[rb] = mma32(QF[m], Sb[m], O[rb]);
+      for (int nb = 0; nb < NB; ++nb) {
+        O[nb][rb] = zero;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) O[nb][rb] = mma32(Sb[nb][m], QF[m], O[nb][rb]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[nb][rb][r] *= egt;
+      }
     }
   }
-  // R = beta (V - e^G K S^T) in place of X, and the e^G Q S^T part of O
+  // R = beta (V - e^G K S^T) in place of X
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const float4 eg = *reinterpret_cast<const float4*>(sEG + 16 * rb + 4 * g4);
     const float4 bi = *reinterpret_cast<const float4*>(sB + 16 * rb + 4 * g4);
-    const bf16x4 vb = __builtin_bit_cast(bf16x4, tr_read(vt + o.V + rb * 32 * BV));
-    X[rb][0] = bi.x * ((float)vb[0] - eg.x * X[rb][0]);
-    X[rb][1] = bi.y * ((float)vb[1] - eg.y * X[rb][1]);
-    X[rb][2] = bi.z * ((float)vb[2] - eg.z * X[rb][2]);
-    X[rb][3] = bi.w * ((float)vb[3] - eg.w * X[rb][3]);
-    if (HAS_OUT) {
-      O[rb][0] *= eg.x;
-      O[rb][1] *= eg.y;
-      O[rb][2] *= eg.z;
-      O[rb][3] *= eg.w;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x4 vb = __builtin_bit_cast(bf16x4, tr_read(vt + o.V[nb] + rb * 32 * BV));
+      X[nb][rb][0] = bi.x * ((float)vb[0] - eg.x * X[nb][rb][0]);
+      X[nb][rb][1] = bi.y * ((float)vb[1] - eg.y * X[nb][rb][1]);
+      X[nb][rb][2] = bi.z * ((float)vb[2] - eg.z * X[nb][rb][2]);
+      X[nb][rb][3] = bi.w * ((float)vb[3] - eg.w * X[nb][rb][3]);
     }
   }
   // block substitution with the helpers' -A_bm and (I + A_bb)^{-1}
@@ -620,67 +685,77 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
   for (int k = 0; k < 6; ++k) nA[k] = lds_at<bf16x4>(pr + pNA + k * 512, lane * 8);
 #pragma unroll
   for (int b = 0; b < 4; ++b) DI[b] = lds_at<bf16x4>(pr + pDI + b * kDIS, lane * 8);
-  f32x4 Vt[4];
-  bf16x4 Vb[4];
-  {
-    Vt[0] = mma16(DI[0], to_bf4(X[0]), zero);
-    Vb[0] = to_bf4(Vt[0]);
-    f32x4 y = mma16(nA[0], Vb[0], X[1]);
-    Vt[1] = mma16(DI[1], to_bf4(y), zero);
-    Vb[1] = to_bf4(Vt[1]);
-    y = mma16(nA[1], Vb[0], X[2]);
-    y = mma16(nA[2], Vb[1], y);
-    Vt[2] = mma16(DI[2], to_bf4(y), zero);
-    Vb[2] = to_bf4(Vt[2]);
-    y = mma16(nA[3], Vb[0], X[3]);
-    y = mma16(nA[4], Vb[1], y);
-    y = mma16(nA[5], Vb[2], y);
-    Vt[3] = mma16(DI[3], to_bf4(y), zero);
-    Vb[3] = to_bf4(Vt[3]);
+  f32x4 Vt[NB][4];
+  bf16x4 Vb[NB][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    Vt[nb][0] = mma16(DI[0], to_bf4(X[nb][0]), zero);
+    Vb[nb][0] = to_bf4(Vt[nb][0]);
+    f32x4 y = mma16(nA[0], Vb[nb][0], X[nb][1]);
+    Vt[nb][1] = mma16(DI[1], to_bf4(y), zero);
+    Vb[nb][1] = to_bf4(Vt[nb][1]);
+    y = mma16(nA[1], Vb[nb][0], X[nb][2]);
+    y = mma16(nA[2], Vb[nb][1], y);
+    Vt[nb][2] = mma16(DI[2], to_bf4(y), zero);
+    Vb[nb][2] = to_bf4(Vt[nb][2]);
+    y = mma16(nA[3], Vb[nb][0], X[nb][3]);
+    y = mma16(nA[4], Vb[nb][1], y);
+    y = mma16(nA[5], Vb[nb][2], y);
+    Vt[nb][3] = mma16(DI[3], to_bf4(y), zero);
+    Vb[nb][3] = to_bf4(Vt[nb][3]);
   }
   if (HAS_OUT) {
-    // O += P Vt over pairs of 16-token blocks (blocks of P above the diagonal are zero)
+    // O^T += Vt^T P^T over pairs of 16-token blocks (blocks of P above the
+    // diagonal are zero; the helpers' P fragments are the B operands)
+    const unsigned char* pp = smem + Cfg<BV>::oPP + (it % 3) * kPP;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
       for (int mp = 0; mp < 2; ++mp) {
         if (2 * mp > rb) continue;
         const int pair = (rb <= 1 ? rb : 2 * rb - 2) + mp;
-        const bf16x8 pa = lds_at<bf16x8>(pr + pP + pair * 1024, lane * 16);
-        O[rb] = mma32(pa, cat8b(Vb[2 * mp], Vb[2 * mp + 1]), O[rb]);
+        const bf16x8 pb = lds_at<bf16x8>(pp + pair * 1024, lane * 16);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) O[nb][rb] = mma32(cat8b(Vb[nb][2 * mp], Vb[nb][2 * mp + 1]), pb, O[nb][rb]);
       }
     }
+    // lane (l16, g4) holds columns 4 g4 .. 4 g4 + 3 of block nb for token 16 rb + l16
+    const unsigned ccol = (unsigned)h * a.Dv + (unsigned)(v0w + 4 * g4);
     if (a.out_all && n == kChunk) {  // every token of a full chunk is an output row, in stream order
-      __bf16* ob = a.out + ((unsigned)t0 + 4 * g4) * HDv + hcol;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ob[(16 * rb + r) * HDv] = (__bf16)O[rb][r];
+        for (int nb = 0; nb < NB; ++nb)
+          *reinterpret_cast<bf16x4*>(a.out + ((unsigned)t0 + 16 * rb + l16) * HDv + ccol + 16 * nb) = to_bf4(O[nb][rb]);
     } else {
       const int* sOR = reinterpret_cast<const int*>(tb + tOR);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        const int4 orow = *reinterpret_cast<const int4*>(sOR + 16 * rb + 4 * g4);
-        const int ors[4] = {orow.x, orow.y, orow.z, orow.w};
+        const int orow = sOR[16 * rb + l16];
+        if (orow >= 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (ors[r] >= 0) a.out[(unsigned)ors[r] * HDv + hcol] = (__bf16)O[rb][r];
+          for (int nb = 0; nb < NB; ++nb)
+            *reinterpret_cast<bf16x4*>(a.out + (unsigned)orow * HDv + ccol + 16 * nb) = to_bf4(O[nb][rb]);
+        }
       }
     }
   }
   if (a.pv) {
-    float* pvb = a.pv + ((unsigned)t0 + 4 * g4) * HDv + hcol;
-    if (n == kChunk) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+    for (int nb = 0; nb < NB; ++nb) {
+      float* pvb = a.pv + ((unsigned)t0 + 4 * g4) * HDv + (unsigned)h * a.Dv + (unsigned)(v0w + 16 * nb + l16);
+      if (n == kChunk) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pvb[(16 * rb + r) * HDv] = Vt[rb][r];
-    } else {
+        for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+          for (int r = 0; r < 4; ++r) pvb[(16 * rb + r) * HDv] = Vt[nb][rb][r];
+      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (16 * rb + 4 * g4 + r < n) pvb[(16 * rb + r) * HDv] = Vt[rb][r];
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * rb + 4 * g4 + r < n) pvb[(16 * rb + r) * HDv] = Vt[nb][rb][r];
+      }
     }
   }
   // states after requested tokens (fork slots, state rows) and at the chunk exit
@@ -693,18 +768,16 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
     // masked, decayed pseudo-values exp(G_p - G_j) vt_j for j ancestor-or-self of p
     // (zero past p, so the product over tokens 32..63 adds nothing when p < 32);
     // on a chain the last token takes the exit decay table (zero past n)
-    bf16x4 Wb[4];
+    float dec[4][4];
     if (!mode && p == n - 1) {
       const float* sDX = reinterpret_cast<const float*>(tb + tDX);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const float4 dx = *reinterpret_cast<const float4*>(sDX + 16 * mb + 4 * g4);
-        f32x4 wv;
-        wv[0] = Vt[mb][0] * dx.x;
-        wv[1] = Vt[mb][1] * dx.y;
-        wv[2] = Vt[mb][2] * dx.z;
-        wv[3] = Vt[mb][3] * dx.w;
-        Wb[mb] = to_bf4(wv);
+        dec[mb][0] = dx.x;
+        dec[mb][1] = dx.y;
+        dec[mb][2] = dx.z;
+        dec[mb][3] = dx.w;
       }
     } else {
       const unsigned mlo = reinterpret_cast<const unsigned*>(tb + tMl)[p];
@@ -715,19 +788,30 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
         const float4 g2 = *reinterpret_cast<const float4*>(sG2 + 16 * mb + 4 * g4);
         const float gj[4] = {g2.x, g2.y, g2.z, g2.w};
         const unsigned mword = mb >= 2 ? mhi : mlo;
-        f32x4 wv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * mb + 4 * g4 + r;
           const bool anc = mode ? ((mword >> (j & 31)) & 1u) : (j <= p);
-          wv[r] = anc ? Vt[mb][r] * __builtin_amdgcn_exp2f(g2p - gj[r]) : 0.f;
+          dec[mb][r] = anc ? __builtin_amdgcn_exp2f(g2p - gj[r]) : 0.f;
         }
-        Wb[mb] = to_bf4(wv);
       }
     }
+    bf16x8 w01[NB], w23[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      bf16x4 Wb[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        f32x4 wv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wv[r] = Vt[nb][mb][r] * dec[mb][r];
+        Wb[mb] = to_bf4(wv);
+      }
+      w01[nb] = cat8b(Wb[0], Wb[1]);
+      w23[nb] = cat8b(Wb[2], Wb[3]);
+    }
     const float cS = sEG[p];
-    const bf16x8 w01 = cat8b(Wb[0], Wb[1]), w23 = cat8b(Wb[2], Wb[3]);
-    f32x4 acc[8];
+    f32x4 acc[NB][8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       // A operand: K^T rows (d_k) of this state block against tokens 0..31 and 32..63
@@ -735,9 +819,12 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
       const bf16x8 k01 = cat8(tr_read(kp), tr_read(kp + 4096));
       const bf16x8 k23 = cat8(tr_read(kp + 8192), tr_read(kp + 8192 + 4096));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[dt][r] = cS * ST[dt][r];
-      acc[dt] = mma32(k01, w01, acc[dt]);
-      acc[dt] = mma32(k23, w23, acc[dt]);
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nb][dt][r] = cS * ST[nb][dt][r];
+        acc[nb][dt] = mma32(k01, w01[nb], acc[nb][dt]);
+        acc[nb][dt] = mma32(k23, w23[nb], acc[nb][dt]);
+      }
     }
     const int fs = reinterpret_cast<const int*>(tb + tFS)[p];
     const int sr = reinterpret_cast<const int*>(tb + tSR)[p];
@@ -745,30 +832,61 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
     if (fs >= 0) {
       float* dst = a.fork_states + ((size_t)fs * a.H + h) * SS + roff;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<f32x4*>(dst + 32 * (dt >> 1) + 4 * (dt & 1)) = acc[dt];
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<f32x4*>(dst + 16 * nb * DK + 32 * (dt >> 1) + 4 * (dt & 1)) = acc[nb][dt];
     }
     if (sr >= 0) {
       float* dst = a.state_out + ((size_t)sr * a.H + h) * SS + roff;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<f32x4*>(dst + 32 * (dt >> 1) + 4 * (dt & 1)) = acc[dt];
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<f32x4*>(dst + 16 * nb * DK + 32 * (dt >> 1) + 4 * (dt & 1)) = acc[nb][dt];
     }
     if (need_exit && p == n - 1) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) ST[dt] = acc[dt];
+      for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) Sb[m] = cat8b(to_bf4(ST[2 * m]), to_bf4(ST[2 * m + 1]));
+        for (int dt = 0; dt < 8; ++dt) ST[nb][dt] = acc[nb][dt];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) Sb[nb][m] = cat8b(to_bf4(ST[nb][2 * m]), to_bf4(ST[nb][2 * m + 1]));
+      }
     }
   } while (todo);
+}
+
+// Entry state rows of the wave's columns (or zeros) in the accumulator layout.
+template <int NB>
+__device__ __forceinline__ void load_entry(const Desc* dp, int ws, int lane, f32x4 (&T)[NB][8]) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const unsigned long long sp = (unsigned long long)dp->sin;
+  const float* sin = (const float*)(((unsigned long long)(unsigned)rfl((int)(sp >> 32)) << 32) | (unsigned)rfl((int)sp));
+  if (sin) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float* row = sin + (size_t)(16 * NB * ws + 16 * nb + l16) * DK + 8 * g4;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        T[nb][dt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 32 * (dt >> 1) + 4 * (dt & 1)));
+    }
+  } else {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) T[nb][dt] = zero;
+  }
 }
 
 template <int BV>
 __device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, int ws, int lane) {
   using C = Cfg<BV>;
+  constexpr int NB = C::NB;
   const int g4 = lane >> 4, l16 = lane & 15;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  SOff o;
+  SOff<NB> o;
 #pragma unroll
   for (int m = 0; m < 4; ++m) o.F[m] = l16 * 256 + (((4 * m + g4) ^ kq_swz(l16)) << 4);
   // lane i of a 16-lane group receives d_k column 32 m + 8 (i / 4) + 4 bb + i % 4 of
@@ -778,16 +896,20 @@ __device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, i
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o.KT[dt] = r0 * 256 + ((((4 * (dt >> 1) + p) ^ kq_swz(r0))) << 4) + ((dt & 1) << 3);
   }
-  {
-    const int vrow = 4 * g4 + (l16 >> 2), vcol = 16 * ws + (l16 & 3) * 4;
-    o.V = vrow * BV * 2 + (((vcol >> 3) ^ v_swz<BV>(vrow)) << 4) + ((vcol & 7) << 1);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int vrow = 4 * g4 + (l16 >> 2), vcol = 16 * NB * ws + 16 * nb + (l16 & 3) * 4;
+    o.V[nb] = vrow * BV * 2 + (((vcol >> 3) ^ v_swz<BV>(vrow)) << 4) + ((vcol & 7) << 1);
   }
-  f32x4 ST[8];
-  bf16x8 Sb[4];
+  f32x4 ST[NB][8];
+  bf16x8 Sb[NB][4];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) ST[dt] = zero;
+  for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) Sb[m] = cat8b(to_bf4(zero), to_bf4(zero));
+    for (int dt = 0; dt < 8; ++dt) ST[nb][dt] = zero;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Sb[nb][m] = cat8b(to_bf4(zero), to_bf4(zero));
+  }
 
   lds_barrier();  // the helpers' iteration -1
   for (int it = 0;; ++it) {
@@ -802,28 +924,19 @@ __device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, i
     const unsigned char* kq = smem + C::oKQ + (it % 3) * 32768;
     const unsigned char* vt = smem + C::oV + (it & 1) * C::VT;
     const unsigned char* pr = smem + C::oPR + (it & 1) * kPR;
-    const int v0w = v0 + 16 * ws;  // first column of the wave
+    const int v0w = v0 + 16 * NB * ws;  // first column of the wave
 
-    if (first) {
-      const unsigned long long sp = (unsigned long long)dp->sin;
-      const float* sin = (const float*)(((unsigned long long)(unsigned)rfl((int)(sp >> 32)) << 32) | (unsigned)rfl((int)sp));
-      if (sin) {
-        const float* row = sin + (size_t)(16 * ws + l16) * DK + 8 * g4;
-        f32x4 t[8];
+    if (first) {  // a new item: its entry state
+      load_entry<NB>(dp, ws, lane, ST);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          t[dt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 32 * (dt >> 1) + 4 * (dt & 1)));
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) ST[dt] = t[dt];
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) ST[dt] = zero;
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) Sb[m] = cat8b(to_bf4(ST[2 * m]), to_bf4(ST[2 * m + 1]));
+        for (int m = 0; m < 4; ++m) Sb[nb][m] = cat8b(to_bf4(ST[nb][2 * m]), to_bf4(ST[nb][2 * m + 1]));
     }
-    if (has_out) state_chunk<BV, true>(a, tb, kq, vt, pr, o, ST, Sb, t0, n, h, v0w, mode, need_exit, todo, lane);
-    else state_chunk<BV, false>(a, tb, kq, vt, pr, o, ST, Sb, t0, n, h, v0w, mode, need_exit, todo, lane);
+    if (has_out)
+      state_chunk<BV, true>(a, smem, tb, kq, vt, pr, o, ST, Sb, it, t0, n, h, v0w, mode, need_exit, todo, lane);
+    else
+      state_chunk<BV, false>(a, smem, tb, kq, vt, pr, o, ST, Sb, it, t0, n, h, v0w, mode, need_exit, todo, lane);
     lds_barrier();
   }
 }
@@ -845,10 +958,10 @@ __global__ void __launch_bounds__(Cfg<BV>::NTHR, 1) k_walk_pipe(const Args a) {
   const int hid = w - C::NS;  // 0 or 1 on the helpers
 
   // Pairs of P whose second 16-token block lies above the diagonal ((0, 1) and
-  // (2, 3)) are never written: clear them once in both product buffers.
-  for (int e = tid; e < 2 * 2 * 64; e += C::NTHR) {
+  // (2, 3)) are never written: clear them once in every P buffer.
+  for (int e = tid; e < 3 * 2 * 64; e += C::NTHR) {
     const int slot = e >> 7, which = (e >> 6) & 1, ln = e & 63;
-    *reinterpret_cast<uint2*>(smem + C::oPR + slot * kPR + pP + (which ? 3 : 0) * 1024 + ln * 16 + 8) = make_uint2(0, 0);
+    *reinterpret_cast<uint2*>(smem + C::oPP + slot * kPP + (which ? 3 : 0) * 1024 + ln * 16 + 8) = make_uint2(0, 0);
   }
 
   // ---- prologue: describe chunks 0 and 1 and copy K, Q and the token tables
