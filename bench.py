@@ -9,7 +9,10 @@ cache cannot hold the next step's operands.
 
 Prints one JSON line (last line of stdout). Progress goes to stderr.
 
-  python bench.py [--steps K] [--warmup W] [--config {1,2,3,4}] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+The default workload is 4 chains of 4096 tokens, 16 heads, d_k = d_v = 128;
+decision_round, draft_trees and mixed_forest are the other full-size streams.
 """
 from __future__ import annotations
 
@@ -114,10 +117,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--workload", default="chains", choices=["chains", "decision_round", "draft_trees", "mixed_forest"])
     ap.add_argument("--rotate", type=int, default=3, help="independent input sets cycled between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (calibrates memory counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -135,7 +140,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     t0 = time.time()
-    wl = W.get_config(args.config)
+    wl = W.get(args.workload)
     log(f"workload {wl.name}: T={wl.T} H={wl.H} Dk={wl.Dk} Dv={wl.Dv} n_seq={wl.n_seq} "
         f"({time.time() - t0:.1f} s to draw) {wl.info}")
     cap = B.capacities(wl.parent, wl.seq_start)
@@ -252,7 +257,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(walk_tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(walk_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
-    roof.update({"kernel": "k_walk", "launches_per_step": cap["max_levels"], "ms_per_step": round(ms_walk, 5),
+    roof.update({"kernel": "k_walk_pipe" if wl.dtype == "bf16" and wl.Dk == 128 else "k_walk", "launches_per_step": cap["max_levels"], "ms_per_step": round(ms_walk, 5),
                  "alg_bytes": cnt["bytes"], "alg_flops": cnt["flops"],
                  "mfma_frac": round(walk_tflops / BF16_PEAK_TFLOPS, 4),
                  "hbm_frac": round(walk_gbs / HBM_PEAK_GBS, 4)})
@@ -291,6 +296,18 @@ def main():
         parity["tol"] = 1e-2 if wl.dtype == "bf16" else 1e-4
         parity["ok"] = all(v <= parity["tol"] for k, v in parity.items() if k not in ("tol",))
         log(f"parity vs oracle: {parity}")
+
+    if args.copy_probe_mib > 0:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
+        # under rocprofv3 --pmc calibrate the walk's counters
+        nb = args.copy_probe_mib << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 3 copies of {nb} bytes")
+        del src, dst
 
     value = wl.T / (ms_step * 1e-3)
     line = {

@@ -99,7 +99,7 @@ def test_capacities_match_reference_planner():
     from oracle import plan as P
     from tree_forked_gated_amd import binding as B
     from tree_forked_gated_amd import workloads as W
-    for wl in [W.config0(), W.random_small(3, n_seq=6, max_len=300), W.config4(total=6000, H=1, D=32)]:
+    for wl in [W.tiny_tree(), W.random_small(3, n_seq=6, max_len=300), W.mixed_forest(total=6000, H=1, D=32)]:
         ref = P.plan(wl.parent, wl.seq_start)
         cap = B.capacities(wl.parent, wl.seq_start)
         assert cap["max_forks"] == ref["n_fork"]

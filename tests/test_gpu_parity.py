@@ -31,9 +31,9 @@ def _check(wl, name, dv_tile=0, pseudo=True):
     return res, ref
 
 
-def test_config0_tiny_tree_fp32():
-    wl = W.config0()
-    res, ref = _check(wl, "config0")
+def test_tiny_tree_fp32():
+    wl = W.tiny_tree()
+    res, ref = _check(wl, "tiny_tree")
     # the five leaf states of the workload
     assert res.state.shape[0] == 5
 
@@ -51,28 +51,28 @@ def test_random_bf16(seed, Dk, Dv):
 
 
 def test_chains_bf16():
-    wl = W.config1(n_seq=3, L=333, H=3, D=128)
+    wl = W.chains(n_seq=3, L=333, H=3, D=128)
     _check(wl, "chains")
 
 
 def test_decision_round_bf16():
-    wl = W.config2(n_req=2, trunk=300, n_branch=5, blen=32, H=2, D=128)
+    wl = W.decision_round(n_req=2, trunk=300, n_branch=5, blen=32, H=2, D=128)
     _check(wl, "decision")
 
 
 def test_draft_trees_bf16():
-    wl = W.config3(n_seq=8, n_nodes=64, H=2, D=128)
+    wl = W.draft_trees(n_seq=8, n_nodes=64, H=2, D=128)
     _check(wl, "draft")
 
 
 def test_mixed_forest_bf16():
-    wl = W.config4(total=4000, H=2, D=128, trunk_range=(100, 900), branch_count=(1, 12), branch_len=(1, 90))
+    wl = W.mixed_forest(total=4000, H=2, D=128, trunk_range=(100, 900), branch_count=(1, 12), branch_len=(1, 90))
     _check(wl, "mixed")
 
 
 @pytest.mark.parametrize("n_nodes", [1, 2, 17, 63, 64])
 def test_tree_chunk_sizes_fp32(n_nodes):
-    wl = W.config3(n_seq=3, n_nodes=n_nodes, H=1, D=16)
+    wl = W.draft_trees(n_seq=3, n_nodes=n_nodes, H=1, D=16)
     wl.dtype = "f32"
     _check(wl, f"tree{n_nodes}")
 

@@ -32,9 +32,9 @@ def _compare(parent, seq_start, **kw):
     return got, ref
 
 
-def test_plan_config0():
-    wl = W.config0()
-    say("plan config0")
+def test_plan_tiny_tree():
+    wl = W.tiny_tree()
+    say("plan tiny_tree")
     got, _ = _compare(wl.parent, wl.seq_start)
     assert got["seg_start"].tolist() == [0, 40, 48, 56, 64]
 
@@ -47,18 +47,18 @@ def test_plan_random(seed):
 
 
 def test_plan_draft_trees_and_forests():
-    wl = W.config3(n_seq=16, n_nodes=64, H=1, D=32)
-    say("plan config3 structure")
+    wl = W.draft_trees(n_seq=16, n_nodes=64, H=1, D=32)
+    say("plan draft_trees structure")
     _compare(wl.parent, wl.seq_start)
-    wl = W.config4(total=20000, H=1, D=32)
-    say(f"plan config4-shaped structure T={wl.T}")
+    wl = W.mixed_forest(total=20000, H=1, D=32)
+    say(f"plan mixed_forest-shaped structure T={wl.T}")
     _compare(wl.parent, wl.seq_start)
 
 
 def test_plan_full_size_structures():
-    for n, kw in [(2, {}), (4, {})]:
-        wl = W.get_config(n, H=1, D=32)
-        say(f"plan full-size structure config{n} T={wl.T}")
+    for name in ["decision_round", "mixed_forest"]:
+        wl = W.get(name, H=1, D=32)
+        say(f"plan full-size structure {name} T={wl.T}")
         _compare(wl.parent, wl.seq_start)
 
 

@@ -153,7 +153,7 @@ def test_closed_form_matches_walk_fp64(seed):
 
 def test_closed_form_matches_walk_fp32():
     """Same check for the fp32 build: the pages report ~1e-7 for fp32."""
-    wl = W.config0()
+    wl = W.tiny_tree()
     r = oracle.forward(wl, "f32")
     lp = wl.parent
     o, pv, _ = cf.tree_wy(lp, wl.q[:, 0], wl.k[:, 0], wl.v[:, 0], wl.beta[:, 0], wl.log_gate[:, 0],
@@ -165,7 +165,7 @@ def test_closed_form_matches_walk_fp32():
 def test_chain_matches_matrix_form_of_eq1():
     """On a chain the walk equals Eq. 1 written with the explicit transition
     alpha (I - beta k k^T) (a different order of operations)."""
-    wl = W.config1(n_seq=1, L=40, H=2, D=8)
+    wl = W.chains(n_seq=1, L=40, H=2, D=8)
     r = oracle.forward(wl, "f64")
     for h in range(wl.H):
         S = wl.init_state[0, h].astype(np.float64)
@@ -193,7 +193,7 @@ def _branch_alone(wl, r_states, fork_tok, branch):
 def test_fork_exactness_bitwise(prec):
     """Flide Prop. 3.1: a branch inside the tree computes exactly what it
     computes alone from its trunk's state (bitwise in the oracle)."""
-    wl = W.config0()
+    wl = W.tiny_tree()
     r = oracle.forward(wl, prec, state_rows=np.array([15, 31], np.int32))
     for fork, branch in [(31, list(range(40, 48))), (31, list(range(56, 64))), (15, list(range(64, 68))),
                          (31, list(range(32, 40)))]:
@@ -236,9 +236,9 @@ def test_no_sibling_leak_and_negative_control():
     """Perturbing sibling branches changes nothing in a branch (bitwise);
     gluing the branch after its siblings as one chain (the delimiter-style
     layout Flide argues against) does change it."""
-    wl = W.config0()
+    wl = W.tiny_tree()
     r = oracle.forward(wl, "f64")
-    pert = W.config0()
+    pert = W.tiny_tree()
     rng = np.random.default_rng(0)
     sib = list(range(40, 64))  # branches 1..3 off token 31
     pert.v[sib] += rng.standard_normal(pert.v[sib].shape)
@@ -251,7 +251,7 @@ def test_no_sibling_leak_and_negative_control():
     glued = wl.parent.copy()
     glued[48] = 47
     glued[56] = 55
-    wg = W.config0()
+    wg = W.tiny_tree()
     wg.parent = glued
     rg = oracle.forward(wg, "f64")
     diff = np.abs(rg["out"][56:64] - r["out"][56:64]).max()
@@ -261,7 +261,7 @@ def test_no_sibling_leak_and_negative_control():
 def test_commit_replay_matches_eq3_and_forward_state():
     """Commit: replaying the accepted path equals Eq. 3 rebuilt from the
     forward's pseudo-values, and equals the forward's own state at the node."""
-    wl = W.config3(n_seq=4, n_nodes=20, H=2, D=16)
+    wl = W.draft_trees(n_seq=4, n_nodes=20, H=2, D=16)
     r = oracle.forward(wl, "f64", state_rows=np.arange(wl.T, dtype=np.int32))
     c = oracle.commit(wl, "f64")
     for p in range(wl.n_path):
@@ -274,19 +274,19 @@ def test_commit_replay_matches_eq3_and_forward_state():
 
 
 def test_commit_empty_path_is_initial_state():
-    wl = W.config3(n_seq=2, n_nodes=10, H=1, D=16)
+    wl = W.draft_trees(n_seq=2, n_nodes=10, H=1, D=16)
     c = oracle.commit(wl, "f64", path_ptr=np.array([0, 0], np.int32), path_nodes=np.zeros(0, np.int32),
                       path_seq=np.array([1], np.int32))
     assert np.array_equal(c[0], wl.init_state[1])
 
 
 def test_oracle_rejects_bad_structure():
-    wl = W.config0()
+    wl = W.tiny_tree()
     wl.parent = wl.parent.copy()
     wl.parent[10] = 10
     with pytest.raises(ValueError):
         oracle.forward(wl, "f64")
-    wl = W.config3(n_seq=2, n_nodes=10, H=1, D=16)
+    wl = W.draft_trees(n_seq=2, n_nodes=10, H=1, D=16)
     with pytest.raises(ValueError):
         oracle.commit(wl, "f64", path_ptr=np.array([0, 1], np.int32), path_nodes=np.array([12], np.int32),
                       path_seq=np.array([0], np.int32))

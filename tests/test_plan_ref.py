@@ -6,11 +6,11 @@ from oracle import plan as P
 from tree_forked_gated_amd import workloads as W
 
 
-def test_config0_plan_by_hand():
+def test_tiny_tree_plan_by_hand():
     """Config-0 tree: the first branch directly follows the trunk's last token
     (parent = t - 1), so it continues the trunk's segment; the other three
     branches off token 31 and the branch off token 15 start segments."""
-    wl = W.config0()
+    wl = W.tiny_tree()
     p = P.plan(wl.parent, wl.seq_start)
     assert p["error"] == (0, 0)
     assert p["seg_start"].tolist() == [0, 40, 48, 56, 64]
@@ -83,7 +83,7 @@ def test_plan_invariants_random(seed):
     ({"seq": {1: 200}}, P.DEV_SEQ_START, 1),
 ])
 def test_plan_errors(bad, code, idx):
-    wl = W.config3(n_seq=3, n_nodes=64, H=1, D=16)
+    wl = W.draft_trees(n_seq=3, n_nodes=64, H=1, D=16)
     parent = wl.parent.copy()
     seq = wl.seq_start.copy()
     for t, v in bad.get("parent", {}).items():
@@ -94,7 +94,7 @@ def test_plan_errors(bad, code, idx):
 
 
 def test_plan_capacity_and_rows_errors():
-    wl = W.config0()
+    wl = W.tiny_tree()
     assert P.plan(wl.parent, wl.seq_start, max_forks=1)["error"] == (P.DEV_FORK_CAPACITY, 31)
     assert P.plan(wl.parent, wl.seq_start, max_levels=1)["error"] == (P.DEV_LEVEL_CAPACITY, 40)
     assert P.plan(wl.parent, wl.seq_start, out_rows=np.array([3, 3]))["error"] == (P.DEV_ROWS, 1)

@@ -75,13 +75,10 @@ unsigned long long plan_fingerprint(const gdn_tree_fwd_args& a);
 hipError_t launch_walk(const gdn_tree_fwd_args& a, const Meta& m, int bv, hipStream_t s);
 hipError_t launch_commit(const gdn_tree_commit_args& a, unsigned long long* err, hipStream_t s);
 bool walk_supported(int dtype, int dk, int bv);
-// MFMA walk for bf16 inputs with d_k = 128 (d_v tiles of 16, 32 or 64 columns)
-bool walk_mfma_supported(int dtype, int dk, int bv);
-bool walk_mfma_fits(const gdn_tree_dims& d);  // sizes within its 32-bit offsets
-hipError_t launch_walk_mfma(const gdn_tree_fwd_args& a, const Meta& m, int bv, hipStream_t s);
-// pipelined MFMA walk (state waves + helper waves), same coverage
+// Pipelined MFMA walk for bf16 inputs with d_k = 128 (d_v tiles of 16, 32 or 64
+// columns): state waves plus helper waves
 bool walk_pipe_supported(int dtype, int dk, int bv);
-bool walk_pipe_fits(const gdn_tree_dims& d);
+bool walk_pipe_fits(const gdn_tree_dims& d);  // sizes within its 32-bit offsets
 hipError_t launch_walk_pipe(const gdn_tree_fwd_args& a, const Meta& m, int bv, hipStream_t s);
 int walk_lds_bytes(int dtype, int dk, int bv);
 

@@ -547,7 +547,6 @@ int walk_lds_bytes(int dtype, int dk, int bv) {
 
 hipError_t launch_walk(const gdn_tree_fwd_args& fa, const Meta& m, int bv, hipStream_t s) {
   if (walk_pipe_supported(fa.dims.dtype, fa.dims.Dk, bv) && walk_pipe_fits(fa.dims)) return launch_walk_pipe(fa, m, bv, s);
-  if (walk_mfma_supported(fa.dims.dtype, fa.dims.Dk, bv) && walk_mfma_fits(fa.dims)) return launch_walk_mfma(fa, m, bv, s);
   WalkArgs wa;
   wa.q = fa.q;
   wa.k = fa.k;

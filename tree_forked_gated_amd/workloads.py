@@ -143,7 +143,7 @@ def _init(rng, n_seq, H, Dv, Dk, random_init):
 
 # --------------------------------------------------------------------- configs
 
-def config0(seed: int = 1000) -> Workload:
+def tiny_tree(seed: int = 1000) -> Workload:
     """Tiny fp32 tree: trunk of 32, four 8-token branches off the trunk's last
     token, one 4-token branch off trunk token 15 (0-based stream index)."""
     rng = np.random.default_rng(seed)
@@ -162,11 +162,11 @@ def config0(seed: int = 1000) -> Workload:
     seq_start = np.array([0, T], dtype=np.int32)
     q, k, v, beta, g = _values(rng, T, H, D, D, "f32")
     init = _init(rng, 1, H, D, D, False)
-    return Workload("config0_tiny_tree_f32", "f32", parent, seq_start, q, k, v, beta, g, init,
+    return Workload("tiny_tree_f32", "f32", parent, seq_start, q, k, v, beta, g, init,
                     None, leaves_of(parent), info={"structure": "trunk 32 + 4x8 off 31 + 4 off 15"})
 
 
-def config1(seed: int = 1001, n_seq: int = 4, L: int = 4096, H: int = 16, D: int = 128) -> Workload:
+def chains(seed: int = 1001, n_seq: int = 4, L: int = 4096, H: int = 16, D: int = 128) -> Workload:
     """Linear chains: n_seq independent sequences of L tokens, random init states."""
     rng = np.random.default_rng(seed)
     T = n_seq * L
@@ -178,11 +178,11 @@ def config1(seed: int = 1001, n_seq: int = 4, L: int = 4096, H: int = 16, D: int
     q, k, v, beta, g = _values(rng, T, H, D, D, "bf16")
     init = _init(rng, n_seq, H, D, D, True)
     last = (seq_start[1:] - 1).astype(np.int32)
-    return Workload(f"config1_chains_{n_seq}x{L}_h{H}_d{D}", "bf16", parent, seq_start, q, k, v, beta, g,
+    return Workload(f"chains_{n_seq}x{L}_h{H}_d{D}", "bf16", parent, seq_start, q, k, v, beta, g,
                     init, None, last, info={"structure": f"{n_seq} chains x {L}"})
 
 
-def config2(seed: int = 1002, n_req: int = 8, trunk: int = 8192, n_branch: int = 16, blen: int = 32,
+def decision_round(seed: int = 1002, n_req: int = 8, trunk: int = 8192, n_branch: int = 16, blen: int = 32,
             H: int = 16, D: int = 128) -> Workload:
     """Decision round: n_req requests, each a trunk with n_branch question
     branches of blen tokens forking from the trunk's final token. Readout rows
@@ -205,7 +205,7 @@ def config2(seed: int = 1002, n_req: int = 8, trunk: int = 8192, n_branch: int =
     q, k, v, beta, g = _values(rng, T, H, D, D, "bf16")
     init = _init(rng, n_req, H, D, D, False)
     ends = np.array(ends, dtype=np.int32)
-    return Workload(f"config2_decision_{n_req}x({trunk}+{n_branch}x{blen})_h{H}_d{D}", "bf16", parent,
+    return Workload(f"decision_round_{n_req}x({trunk}+{n_branch}x{blen})_h{H}_d{D}", "bf16", parent,
                     seq_start, q, k, v, beta, g, init, ends.copy(), ends.copy(),
                     info={"structure": f"{n_req} x (trunk {trunk} + {n_branch} x {blen})"})
 
@@ -245,7 +245,7 @@ def random_draft_tree(rng, n_nodes: int = 64, max_depth: int = 8, max_fanout: in
     return out
 
 
-def config3(seed: int = 1003, n_seq: int = 64, n_nodes: int = 64, H: int = 32, D: int = 128) -> Workload:
+def draft_trees(seed: int = 1003, n_seq: int = 64, n_nodes: int = 64, H: int = 32, D: int = 128) -> Workload:
     """Draft-tree verify: n_seq random trees of n_nodes over committed random
     states; all outputs and pseudo-values; then one root-to-leaf path per tree."""
     rng = np.random.default_rng(seed)
@@ -266,7 +266,7 @@ def config3(seed: int = 1003, n_seq: int = 64, n_nodes: int = 64, H: int = 32, D
         path = root_path(parent, leaf)
         nodes += path
         ptr.append(len(nodes))
-    wl = Workload(f"config3_draft_{n_seq}x{n_nodes}_h{H}_d{D}", "bf16", parent, seq_start, q, k, v, beta, g,
+    wl = Workload(f"draft_trees_{n_seq}x{n_nodes}_h{H}_d{D}", "bf16", parent, seq_start, q, k, v, beta, g,
                   init, None, np.zeros(0, dtype=np.int32), keep_pseudo=True,
                   path_ptr=np.array(ptr, dtype=np.int32), path_nodes=np.array(nodes, dtype=np.int32),
                   path_seq=np.arange(n_seq, dtype=np.int32),
@@ -297,7 +297,7 @@ def random_forest_tokens(rng, trunk_range=(512, 4096), branch_count=(1, 64), bra
     return np.array(par, dtype=np.int32), np.array(nest, dtype=np.int32)
 
 
-def config4(seed: int = 1004, total: int = 65536, H: int = 32, D: int = 128, all_leaf_states: bool = False,
+def mixed_forest(seed: int = 1004, total: int = 65536, H: int = 32, D: int = 128, all_leaf_states: bool = False,
             **forest_kw) -> Workload:
     """Large mixed stream: seeded random forests (one trunk each, one sequence
     each) appended while they fit; the next one is cut in stream order to reach
@@ -324,7 +324,7 @@ def config4(seed: int = 1004, total: int = 65536, H: int = 32, D: int = 128, all
     lv = leaves_of(parent)
     nest = np.concatenate(nests)
     n_branch = int(np.sum((parent >= 0) & (parent != np.arange(T) - 1)))
-    return Workload(f"config4_mixed_{T}_h{H}_d{D}", "bf16", parent, seq_start, q, k, v, beta, g, init,
+    return Workload(f"mixed_forest_{T}_h{H}_d{D}", "bf16", parent, seq_start, q, k, v, beta, g, init,
                     None, lv if all_leaf_states else np.zeros(0, dtype=np.int32),
                     info={"structure": f"{n_seq} forests, {n_branch} branches, {lv.shape[0]} leaves",
                           "n_forests": n_seq, "n_branches": n_branch, "n_leaves": int(lv.shape[0]),
@@ -362,8 +362,10 @@ def random_small(seed: int, n_seq: int = 3, H: int = 2, Dk: int = 32, Dv: int = 
                     leaves_of(parent))
 
 
-CONFIGS = {0: config0, 1: config1, 2: config2, 3: config3, 4: config4}
+WORKLOADS = {"tiny_tree": tiny_tree, "chains": chains, "decision_round": decision_round, "draft_trees": draft_trees,
+             "mixed_forest": mixed_forest}
 
 
-def get_config(n: int, **kw) -> Workload:
-    return CONFIGS[n](**kw)
+def get(name: str, **kw) -> Workload:
+    """A named workload at its default (full) size, or with sizes overridden."""
+    return WORKLOADS[name](**kw)
