@@ -122,8 +122,8 @@ typedef struct gdn_tree_dims {
 
 /*
  * Arguments of gdn_tree_forward / gdn_tree_plan.
- *  q, k, v, log_gate, beta   inputs in dims.dtype (layouts above)
- *  parent_idx [T] int32      global parent index, -1 = the sequence's initial state;
+ *  q, k, v, log_gate, beta   inputs in dims.dtype (layouts above); may be NULL when T = 0
+ *  parent_idx [T] int32      global parent index, -1 = the sequence's initial state (NULL when T = 0);
  *                            parents precede children (TreeWY section 3: DFS pre-order
  *                            or any parents-first layout; Flide: trunk before its questions)
  *  seq_start [n_seq+1] int32 CSR of the sequences (seq_start[0] = 0, last = T)

@@ -60,7 +60,8 @@ int check_fwd(const gdn_tree_fwd_args* a, bool walk, LayoutFull* L) {
   int rc = check_dims(&a->dims);
   if (rc) return rc;
   const gdn_tree_dims& d = a->dims;
-  if (!a->parent_idx || !a->seq_start || !a->workspace) return fail(GDN_ERR_NULL, "parent_idx, seq_start and workspace are required");
+  if (!a->seq_start || !a->workspace || (d.T > 0 && !a->parent_idx))
+    return fail(GDN_ERR_NULL, "seq_start, workspace and (T > 0) parent_idx are required");
   if (!compute_layout(d, L)) return fail(GDN_ERR_DIMS, "bad sizes");
   if (a->workspace_bytes < L->pub.total) return fail(GDN_ERR_WORKSPACE, "workspace smaller than gdn_tree_workspace_size");
   if (((uintptr_t)a->workspace & 255u) != 0) return fail(GDN_ERR_ARGS, "workspace must be 256-byte aligned");
@@ -69,7 +70,8 @@ int check_fwd(const gdn_tree_fwd_args* a, bool walk, LayoutFull* L) {
   if (a->n_out > 0 && !a->out_rows && a->n_out != d.T) return fail(GDN_ERR_ARGS, "without out_rows, n_out must be T");
   if (a->flags & ~GDN_FWD_PLANNED) return fail(GDN_ERR_ARGS, "unknown flags");
   if (!walk) return GDN_OK;
-  if (!a->q || !a->k || !a->v || !a->log_gate || !a->beta) return fail(GDN_ERR_NULL, "q, k, v, log_gate and beta are required");
+  if (d.T > 0 && (!a->q || !a->k || !a->v || !a->log_gate || !a->beta))
+    return fail(GDN_ERR_NULL, "q, k, v, log_gate and beta are required when T > 0");
   if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out) || !aligned16(a->init_state) ||
       !aligned16(a->state_out) || !aligned16(a->pseudo_v))
     return fail(GDN_ERR_ARGS, "q, k, v, out, init_state, state_out and pseudo_v must be 16-byte aligned");
