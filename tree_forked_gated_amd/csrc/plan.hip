@@ -70,31 +70,50 @@ __global__ void k_init(Meta m, int T, int n_seq, int max_levels) {
   }
 }
 
-// Last kernel of a plan: the metadata is complete for these sizes.
-__global__ void k_plan_done(Meta m, unsigned long long tag) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) *m.plan_tag = tag;
-}
-
 __global__ void k_replan_check(Meta m, int max_levels, unsigned long long tag) {
   for (int i = threadIdx.x; i < max_levels * kWalkQueues; i += blockDim.x) m.walk_ctr[i] = 0;
   if (threadIdx.x == 0 && *m.plan_tag != tag) raise_error(m.err, GDN_DEV_NOT_PLANNED, 0);
 }
 
-__global__ void k_seq_check(const int* seq_start, int n_seq, int T, Meta m) {
-  int s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (s > n_seq) return;
-  int v = seq_start[s];
-  if (s == 0) {
-    if (v != 0) raise_error(m.err, GDN_DEV_SEQ_START, 0);
-    return;
-  }
-  if (v < seq_start[s - 1] || v > T) raise_error(m.err, GDN_DEV_SEQ_START, s);
-  else if (s == n_seq && v != T) raise_error(m.err, GDN_DEV_SEQ_START, s);
+// Per token: sequence, order checks, segment starts and fork flags. The same
+// launch checks seq_start (threads 0..n_seq) and maps the requested rows
+// (threads beyond T). With a bad seq_start its error (the smallest code) is the
+// one reported; the lookups below stay in range whatever seq_start holds.
+__device__ inline void map_row(const int* rows, int n, int i, int T, int* map, unsigned long long* err) {
+  if (i >= n) return;
+  int r = rows[i];
+  if (r < 0 || r >= T) raise_error(err, GDN_DEV_ROWS, i);
+  else atomicMin(&map[r], i);
 }
 
-__global__ void k_tokens(const int* parent, const int* seq_start, int n_seq, int T, Meta m) {
-  int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T || bad_csr(m)) return;
+__device__ inline void check_row(const int* rows, int n, int i, int T, const int* map, unsigned long long* err) {
+  if (i >= n) return;
+  int r = rows[i];
+  if (r >= 0 && r < T && map[r] != i) raise_error(err, GDN_DEV_ROWS, i);
+}
+
+__global__ void k_tokens(const int* parent, const int* seq_start, int n_seq, int T, const int* out_rows, int n_out,
+                         const int* state_rows, int n_state, Meta m) {
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid <= n_seq) {
+    const int s = (int)gid;
+    const int v = seq_start[s];
+    if (s == 0) {
+      if (v != 0) raise_error(m.err, GDN_DEV_SEQ_START, 0);
+    } else if (v < seq_start[s - 1] || v > T) {
+      raise_error(m.err, GDN_DEV_SEQ_START, s);
+    } else if (s == n_seq && v != T) {
+      raise_error(m.err, GDN_DEV_SEQ_START, s);
+    }
+  }
+  if (gid >= T) {
+    const long long i = gid - T;
+    if (out_rows && i < n_out) map_row(out_rows, n_out, (int)i, T, m.out_map, m.err);
+    if (state_rows && i < n_state) map_row(state_rows, n_state, (int)i, T, m.state_map, m.err);
+    return;
+  }
+  if (n_seq <= 0) return;
+  const int t = (int)gid;
   int s = upper_bound_seq(seq_start, n_seq, t);
   m.tok_seq[t] = s;
   int a = seq_start[s], b = seq_start[s + 1];
@@ -111,21 +130,6 @@ __global__ void k_tokens(const int* parent, const int* seq_start, int n_seq, int
   int start = tree ? (t == a) : (p < 0 || p != t - 1);
   m.is_start[t] = start;
   if (!tree && start && ok && p >= 0) m.is_fork[p] = 1;
-}
-
-__global__ void k_rows(const int* rows, int n, int T, int* map, unsigned long long* err) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  int r = rows[i];
-  if (r < 0 || r >= T) raise_error(err, GDN_DEV_ROWS, i);
-  else atomicMin(&map[r], i);
-}
-
-__global__ void k_rows_check(const int* rows, int n, int T, const int* map, unsigned long long* err) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  int r = rows[i];
-  if (r >= 0 && r < T && map[r] != i) raise_error(err, GDN_DEV_ROWS, i);
 }
 
 // ---- exclusive scans of is_start (segment ids) and is_fork (slot ids)
@@ -147,8 +151,17 @@ __device__ inline int block_excl_scan(int v, int* sh, int* total) {
   return incl - v;
 }
 
-__global__ void __launch_bounds__(256) k_scan_reduce(int T, Meta m) {
+// Block totals of the scans; the same launch checks that requested rows are
+// distinct (every mapping is in place once the token launch is done).
+__global__ void __launch_bounds__(256) k_scan_reduce(int T, const int* out_rows, int n_out, const int* state_rows,
+                                                     int n_state, int row_blocks, Meta m) {
   __shared__ int sh[256];
+  if ((int)blockIdx.x >= (int)gridDim.x - row_blocks) {
+    const int i = ((int)blockIdx.x - ((int)gridDim.x - row_blocks)) * 256 + threadIdx.x;
+    if (out_rows) check_row(out_rows, n_out, i, T, m.out_map, m.err);
+    if (state_rows) check_row(state_rows, n_state, i, T, m.state_map, m.err);
+    return;
+  }
   int base = blockIdx.x * kScanTile;
   int a = 0, f = 0;
   for (int i = threadIdx.x; i < kScanTile; i += 256) {
@@ -188,9 +201,39 @@ __global__ void __launch_bounds__(256) k_scan_top(int nb, Meta m) {
   }
 }
 
+// FOLD: the offsets of the preceding blocks are summed here (few blocks);
+// otherwise k_scan_top has written them.
+template <bool FOLD>
 __global__ void __launch_bounds__(256) k_scan_apply(int T, int nb, int max_forks, Meta m) {
   __shared__ int sh[256];
   constexpr int per = kScanTile / 256;
+  int base_a = 0, base_f = 0;
+  if (FOLD) {
+    int pa = 0, pf = 0, qa = 0, qf = 0;  // preceding blocks, all blocks
+    for (int b = threadIdx.x; b < nb; b += 256) {
+      const int sa = m.scan_sums[2 * b], sf = m.scan_sums[2 * b + 1];
+      qa += sa;
+      qf += sf;
+      if (b < (int)blockIdx.x) {
+        pa += sa;
+        pf += sf;
+      }
+    }
+    int t0, t1, t2, t3;
+    block_excl_scan(pa, sh, &t0);
+    block_excl_scan(pf, sh, &t1);
+    block_excl_scan(qa, sh, &t2);
+    block_excl_scan(qf, sh, &t3);
+    base_a = t0;
+    base_f = t1;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      *m.n_seg = t2;
+      *m.n_fork = t3;
+    }
+  } else {
+    base_a = m.scan_sums[2 * nb + 2 * blockIdx.x];
+    base_f = m.scan_sums[2 * nb + 2 * blockIdx.x + 1];
+  }
   int base = blockIdx.x * kScanTile + threadIdx.x * per;
   int a = 0, f = 0;
   for (int i = 0; i < per; ++i) {
@@ -198,8 +241,8 @@ __global__ void __launch_bounds__(256) k_scan_apply(int T, int nb, int max_forks
     if (t < T) { a += m.is_start[t]; f += m.is_fork[t]; }
   }
   int ta, tf;
-  int ea = block_excl_scan(a, sh, &ta) + m.scan_sums[2 * nb + 2 * blockIdx.x];
-  int ef = block_excl_scan(f, sh, &tf) + m.scan_sums[2 * nb + 2 * blockIdx.x + 1];
+  int ea = block_excl_scan(a, sh, &ta) + base_a;
+  int ef = block_excl_scan(f, sh, &tf) + base_f;
   for (int i = 0; i < per; ++i) {
     int t = base + i;
     if (t >= T) break;
@@ -251,56 +294,68 @@ __global__ void k_levels(int max_levels, Meta m) {
   if (lv < max_levels) atomicAdd(&m.level_count[lv], 1);
 }
 
-__global__ void k_level_ptr(int max_levels, Meta m) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int run = 0;
-  for (int l = 0; l < max_levels; ++l) {
-    m.level_ptr[l] = run;
-    run += m.level_count[l];
+// Last launch of a plan. Blocks [0, gT) fill the level lists (thread i takes
+// segment i; the level offsets are an exclusive scan of the level counts, formed
+// by every block) and the depths of chain tokens (thread i takes token i);
+// blocks from gT on take four tree sequences each, one per wave, for their
+// depths and ancestor-or-self masks by pointer jumping (six rounds cover 64
+// levels). Block 0 records the level offsets and the plan's fingerprint.
+__global__ void __launch_bounds__(256) k_finish(const int* parent, const int* seq_start, int T, int n_seq,
+                                                int max_levels, int gT, unsigned long long tag, Meta m) {
+  __shared__ int sh[256];
+  if ((int)blockIdx.x < gT) {
+    extern __shared__ int lptr[];  // [max_levels + 1]
+    int run = 0;
+    for (int c = 0; c < max_levels; c += 256) {
+      const int l = c + threadIdx.x;
+      const int v = l < max_levels ? m.level_count[l] : 0;
+      int tot;
+      const int ex = block_excl_scan(v, sh, &tot);
+      if (l < max_levels) lptr[l] = run + ex;
+      run += tot;
+    }
+    if (threadIdx.x == 0) lptr[max_levels] = run;
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int l = threadIdx.x; l <= max_levels; l += 256) m.level_ptr[l] = lptr[l];
+      if (threadIdx.x == 0) *m.plan_tag = tag;
+    }
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < *m.n_seg) {
+      const int lv = m.seg_level[i];
+      if (lv < max_levels) {
+        const int pos = atomicAdd(&m.level_fill[lv], 1);
+        m.level_items[lptr[lv] + pos] = i;
+        m.unit_info[lptr[lv] + pos] = make_int4(m.seg_start[i], m.seg_len[i], m.seg_mode[i] | (m.seg_seq[i] << 1),
+                                                m.seg_slot[i]);
+      }
+    }
+    if (i < T && !bad_csr(m)) {
+      const int s = m.tok_seq[i];
+      if (seq_start[s + 1] - seq_start[s] > kChunk) {  // tree chunks: below
+        const int j = seg_of(m.seg_start, *m.n_seg, i);
+        m.depth[i] = m.seg_depth0[j] + (i - m.seg_start[j]);
+      }
+    }
+    return;
   }
-  m.level_ptr[max_levels] = run;
-}
-
-__global__ void k_level_fill(int max_levels, Meta m) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= *m.n_seg) return;
-  int lv = m.seg_level[i];
-  if (lv >= max_levels) return;
-  int pos = atomicAdd(&m.level_fill[lv], 1);
-  m.level_items[m.level_ptr[lv] + pos] = i;
-  m.unit_info[m.level_ptr[lv] + pos] = make_int4(m.seg_start[i], m.seg_len[i], m.seg_mode[i] | (m.seg_seq[i] << 1),
-                                                 m.seg_slot[i]);
-}
-
-__global__ void k_depth(const int* seq_start, int T, Meta m) {
-  int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T || bad_csr(m)) return;
-  int s = m.tok_seq[t];
-  if (seq_start[s + 1] - seq_start[s] <= kChunk) return;  // tree chunks: k_tree_meta
-  int j = seg_of(m.seg_start, *m.n_seg, t);
-  m.depth[t] = m.seg_depth0[j] + (t - m.seg_start[j]);
-}
-
-// One wave per sequence: depth and ancestor-or-self masks of a tree chunk by
-// pointer jumping (six rounds cover 64 levels).
-__global__ void __launch_bounds__(64) k_tree_meta(const int* parent, const int* seq_start, Meta m) {
-  int s = blockIdx.x;
-  if (bad_csr(m)) return;
-  int a = seq_start[s], n = seq_start[s + 1] - a;
+  const int s = ((int)blockIdx.x - gT) * 4 + (int)(threadIdx.x >> 6);
+  if (s >= n_seq || bad_csr(m)) return;
+  const int a = seq_start[s], n = seq_start[s + 1] - a;
   if (n <= 0 || n > kChunk) return;
-  int i = threadIdx.x;
+  const int i = threadIdx.x & 63;
   int p = -1;
   if (i < n) {
-    int g = parent[a + i];
+    const int g = parent[a + i];
     p = (g >= a && g < a + i) ? g - a : -1;
   }
   unsigned long long anc = (i < n) ? (1ull << i) : 0ull;
   int d = (p >= 0) ? 1 : 0;
   for (int r = 0; r < 6; ++r) {
-    int src = p >= 0 ? p : i;
-    unsigned long long panc = __shfl(anc, src);
-    int pd = __shfl(d, src);
-    int pp = __shfl(p, src);
+    const int src = p >= 0 ? p : i;
+    const unsigned long long panc = __shfl(anc, src);
+    const int pd = __shfl(d, src);
+    const int pp = __shfl(p, src);
     if (p >= 0) {
       anc |= panc;
       d += pd;
@@ -423,34 +478,34 @@ hipError_t launch_plan(const gdn_tree_fwd_args& a, const Meta& m, const LayoutFu
   if ((long long)ml * kWalkQueues > init_n) init_n = (long long)ml * kWalkQueues;
   if (init_n < 1) init_n = 1;
   const int gT = blocks_for(T > 0 ? T : 1, bs);
+  const int* out_rows = a.n_out > 0 ? a.out_rows : nullptr;
+  const int* state_rows = a.n_state > 0 ? a.state_rows : nullptr;
+  const long long n_rows = (out_rows ? a.n_out : 0) > (state_rows ? a.n_state : 0) ? (out_rows ? a.n_out : 0)
+                                                                                     : (state_rows ? a.n_state : 0);
+  long long tok_threads = (long long)T + n_rows;
+  if (tok_threads < (long long)n_seq + 1) tok_threads = (long long)n_seq + 1;
   hipLaunchKernelGGL(k_init, dim3(blocks_for(init_n, bs)), dim3(bs), 0, s, m, T, n_seq, ml);
-  hipLaunchKernelGGL(k_seq_check, dim3(blocks_for(n_seq + 1, bs)), dim3(bs), 0, s, a.seq_start, n_seq, T, m);
-  if (T > 0 && n_seq > 0)
-    hipLaunchKernelGGL(k_tokens, dim3(gT), dim3(bs), 0, s, a.parent_idx, a.seq_start, n_seq, T, m);
-  if (a.out_rows && a.n_out > 0) {
-    hipLaunchKernelGGL(k_rows, dim3(blocks_for(a.n_out, bs)), dim3(bs), 0, s, a.out_rows, a.n_out, T, m.out_map, m.err);
-    hipLaunchKernelGGL(k_rows_check, dim3(blocks_for(a.n_out, bs)), dim3(bs), 0, s, a.out_rows, a.n_out, T, m.out_map,
-                       m.err);
-  }
-  if (a.state_rows && a.n_state > 0) {
-    hipLaunchKernelGGL(k_rows, dim3(blocks_for(a.n_state, bs)), dim3(bs), 0, s, a.state_rows, a.n_state, T,
-                       m.state_map, m.err);
-    hipLaunchKernelGGL(k_rows_check, dim3(blocks_for(a.n_state, bs)), dim3(bs), 0, s, a.state_rows, a.n_state, T,
-                       m.state_map, m.err);
-  }
-  if (T > 0 && n_seq > 0) {
-    const int nb = L.n_scan_blocks;
-    hipLaunchKernelGGL(k_scan_reduce, dim3(nb), dim3(256), 0, s, T, m);
-    hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(256), 0, s, nb, m);
-    hipLaunchKernelGGL(k_scan_apply, dim3(nb), dim3(256), 0, s, T, nb, a.dims.max_forks, m);
+  hipLaunchKernelGGL(k_tokens, dim3(blocks_for(tok_threads, bs)), dim3(bs), 0, s, a.parent_idx, a.seq_start, n_seq, T,
+                     out_rows, a.n_out, state_rows, a.n_state, m);
+  const int nb = L.n_scan_blocks;
+  const int row_blocks = blocks_for(n_rows, bs);
+  const bool work = T > 0 && n_seq > 0;
+  if (work || row_blocks > 0)
+    hipLaunchKernelGGL(k_scan_reduce, dim3((work ? nb : 0) + row_blocks), dim3(256), 0, s, T, out_rows, a.n_out,
+                       state_rows, a.n_state, row_blocks, m);
+  if (work) {
+    if (nb <= 1024) {
+      hipLaunchKernelGGL(k_scan_apply<true>, dim3(nb), dim3(256), 0, s, T, nb, a.dims.max_forks, m);
+    } else {
+      hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(256), 0, s, nb, m);
+      hipLaunchKernelGGL(k_scan_apply<false>, dim3(nb), dim3(256), 0, s, T, nb, a.dims.max_forks, m);
+    }
     hipLaunchKernelGGL(k_segments, dim3(gT), dim3(bs), 0, s, a.parent_idx, a.seq_start, T, m);
     hipLaunchKernelGGL(k_levels, dim3(gT), dim3(bs), 0, s, ml, m);
-    hipLaunchKernelGGL(k_level_ptr, dim3(1), dim3(64), 0, s, ml, m);
-    hipLaunchKernelGGL(k_level_fill, dim3(gT), dim3(bs), 0, s, ml, m);
-    hipLaunchKernelGGL(k_depth, dim3(gT), dim3(bs), 0, s, a.seq_start, T, m);
-    hipLaunchKernelGGL(k_tree_meta, dim3(n_seq), dim3(64), 0, s, a.parent_idx, a.seq_start, m);
   }
-  hipLaunchKernelGGL(k_plan_done, dim3(1), dim3(64), 0, s, m, tag);
+  const int tree_blocks = work ? blocks_for(n_seq, 4) : 0;
+  hipLaunchKernelGGL(k_finish, dim3(gT + tree_blocks), dim3(bs), 4 * (ml + 1), s, a.parent_idx, a.seq_start, T, n_seq,
+                     ml, gT, tag, m);
   return hipGetLastError();
 }
 
