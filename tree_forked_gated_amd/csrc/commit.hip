@@ -5,7 +5,7 @@
 //
 // g_a / g_i = exp(sum of the log gates strictly after i on the path), summed
 // from a backwards in fp32; g_a = exp of the whole path's sum. One workgroup
-// per (path, head, 16 rows of S): it reads S_0 once, the path's pseudo-values,
+// per (path, head, 32 rows of S): it reads S_0 once, the path's pseudo-values,
 // keys and gates, and writes S_a once. The kernel is bound by those two state
 // streams (HBM), so it stays on plain fp32 FMAs with float4 loads and stores.
 #include "gdn_internal.h"
@@ -13,8 +13,10 @@
 namespace gdn {
 namespace {
 
-constexpr int kRows = 16;   // rows of S per workgroup
-constexpr int kPathTile = 64;
+constexpr int kRows = 32;      // rows of S per workgroup
+constexpr int kPathTile = 16;  // path nodes staged in LDS at a time
+constexpr int kThreads = 256;
+constexpr int kPer4 = kRows * 128 / 4 / kThreads;  // float4 groups of the block per thread (d_k <= 128)
 
 struct CommitArgs {
   const void* k;
@@ -38,65 +40,87 @@ __global__ void k_reset(unsigned long long* err) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *err = kNoError;
 }
 
+// One workgroup per (path, head, 32 rows of S). The rows of S_0 are loaded
+// first, so that they arrive while the path is summed. The path is staged in
+// LDS 16 nodes at a time, from the accepted node backwards: each node is
+// checked (in its sequence, parent = previous node) in the same pass that loads
+// its key, pseudo-values and gate, with the index held in range until the
+// check is decided, just before the stores.
 template <typename E>
-__global__ void __launch_bounds__(256) k_commit(CommitArgs a) {
+__global__ void __launch_bounds__(kThreads, 6) k_commit(CommitArgs a) {
   __shared__ float sK[kPathTile][128 + 4];
   __shared__ float sV[kPathTile][kRows];
+  __shared__ float sG[kPathTile];
   __shared__ float sW[kPathTile];
   __shared__ float sSigma;
   const int p = blockIdx.x, h = blockIdx.y, vb = blockIdx.z;
   const int tid = threadIdx.x;
-  const int seq = a.path_seq[p];
-  const int beg = a.path_ptr[p], end = a.path_ptr[p + 1];
-  bool bad = (seq < 0 || seq >= a.n_seq || end < beg);
-  if (!bad) {
-    const int s0 = a.seq_start[seq], s1 = a.seq_start[seq + 1];
-    for (int j = beg + tid; j < end; j += blockDim.x) {
-      const int t = a.path_nodes[j];
-      const int want = (j == beg) ? -1 : a.path_nodes[j - 1];
-      if (t < s0 || t >= s1 || a.parent[t] != want) bad = true;
-    }
-  }
-  if (__syncthreads_or(bad)) {
-    if (tid == 0) raise_error(a.err, GDN_DEV_PATH, p);
-    return;
-  }
   const int Dk = a.Dk, H = a.H, Dv = a.Dv;
-  const E* kg = reinterpret_cast<const E*>(a.k);
-  const E* gg = reinterpret_cast<const E*>(a.g);
-  // this thread's elements of the 16 x Dk block, four consecutive columns each
   const int per_row4 = Dk / 4;
   const int n4 = kRows * per_row4;  // float4 groups in the block
-  constexpr int kMax4 = kRows * 128 / 4 / 256;  // at most 2 groups per thread
-  float4 acc[kMax4];
-  for (int i = 0; i < kMax4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int rows = min(kRows, Dv - vb * kRows);
+  const size_t SS = (size_t)Dv * Dk;
+  const int seq = a.path_seq[p];
+  const int beg = a.path_ptr[p], end = a.path_ptr[p + 1];
+  const bool bad_path = (seq < 0 || seq >= a.n_seq || end < beg);
+  bool bad = bad_path;
+  // S_0 rows of this block (zeros without initial states)
+  float4 s0[kPer4];
+  const float* S0 = (!bad_path && a.init) ? a.init + ((size_t)seq * H + h) * SS : nullptr;
+#pragma unroll
+  for (int i = 0; i < kPer4; ++i) {
+    const int gidx = tid + kThreads * i;
+    const int r = gidx / per_row4, d = (gidx % per_row4) * 4;
+    s0[i] = (S0 && gidx < n4 && r < rows) ? *reinterpret_cast<const float4*>(S0 + (size_t)(vb * kRows + r) * Dk + d)
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const E* kg = reinterpret_cast<const E*>(a.k);
+  const E* gg = reinterpret_cast<const E*>(a.g);
+  const int s_0 = bad_path ? 0 : a.seq_start[seq], s_1 = bad_path ? 0 : a.seq_start[seq + 1];
+  // a non-empty path needs a non-empty sequence; nothing is loaded otherwise
+  const bool no_tokens = !bad_path && end > beg && s_1 <= s_0;
+  bad |= no_tokens;
+  float4 acc[kPer4];
+#pragma unroll
+  for (int i = 0; i < kPer4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   if (tid == 0) sSigma = 0.f;
   __syncthreads();
-  // walk the path backwards in tiles of 64 nodes
-  for (int tile_end = end; tile_end > beg; tile_end -= kPathTile) {
+  for (int tile_end = (bad_path || no_tokens) ? beg : end; tile_end > beg; tile_end -= kPathTile) {
     const int tile_beg = max(beg, tile_end - kPathTile);
     const int nt = tile_end - tile_beg;
-    for (int idx = tid; idx < nt * Dk; idx += blockDim.x) {
+    if (tid < nt) {  // check the node and load its gate
+      const int j = tile_beg + tid;
+      const int t = a.path_nodes[j];
+      const int want = (j == beg) ? -1 : a.path_nodes[j - 1];
+      const bool ok = t >= s_0 && t < s_1 && a.parent[t] == want;
+      bad |= !ok;
+      sG[tid] = ok ? upc<E>(gg[(size_t)t * H + h]) : 0.f;
+    }
+    for (int idx = tid; idx < nt * Dk; idx += kThreads) {
       const int j = idx / Dk, d = idx % Dk;
-      const int t = a.path_nodes[tile_beg + j];
+      int t = a.path_nodes[tile_beg + j];
+      t = (t >= s_0 && t < s_1) ? t : s_0;  // in range until the check is decided
       sK[j][d] = upc<E>(kg[((size_t)t * H + h) * Dk + d]);
     }
-    for (int idx = tid; idx < nt * kRows; idx += blockDim.x) {
+    for (int idx = tid; idx < nt * kRows; idx += kThreads) {
       const int j = idx / kRows, r = idx % kRows;
-      const int t = a.path_nodes[tile_beg + j];
-      sV[j][r] = a.pv[((size_t)t * H + h) * Dv + vb * kRows + r];
+      int t = a.path_nodes[tile_beg + j];
+      t = (t >= s_0 && t < s_1) ? t : s_0;
+      sV[j][r] = r < rows ? a.pv[((size_t)t * H + h) * Dv + vb * kRows + r] : 0.f;
     }
+    __syncthreads();
     if (tid == 0) {  // weights exp(sum of log gates after node j), accumulated from a backwards
       float sigma = sSigma;
       for (int j = nt - 1; j >= 0; --j) {
         sW[j] = __expf(sigma);
-        sigma += upc<E>(gg[(size_t)a.path_nodes[tile_beg + j] * H + h]);
+        sigma += sG[j];
       }
       sSigma = sigma;
     }
     __syncthreads();
-    for (int i = 0; i < kMax4; ++i) {
-      const int gidx = tid + 256 * i;
+#pragma unroll
+    for (int i = 0; i < kPer4; ++i) {
+      const int gidx = tid + kThreads * i;
       if (gidx < n4) {
         const int r = gidx / per_row4, d = (gidx % per_row4) * 4;
         float4 s = acc[i];
@@ -112,22 +136,23 @@ __global__ void __launch_bounds__(256) k_commit(CommitArgs a) {
     }
     __syncthreads();
   }
+  if (__syncthreads_or(bad)) {
+    if (tid == 0) raise_error(a.err, GDN_DEV_PATH, p);
+    return;
+  }
   const float ga = __expf(sSigma);
-  const size_t SS = (size_t)Dv * Dk;
-  const float* S0 = a.init ? a.init + ((size_t)seq * H + h) * SS : nullptr;
   float* dst = a.out + ((size_t)p * H + h) * SS;
-  for (int i = 0; i < kMax4; ++i) {
-    const int gidx = tid + 256 * i;
-    if (gidx < n4) {
-      const int r = gidx / per_row4, d = (gidx % per_row4) * 4;
-      const size_t off = (size_t)(vb * kRows + r) * Dk + d;
-      float4 s0 = S0 ? *reinterpret_cast<const float4*>(S0 + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < kPer4; ++i) {
+    const int gidx = tid + kThreads * i;
+    const int r = gidx / per_row4, d = (gidx % per_row4) * 4;
+    if (gidx < n4 && r < rows) {
       float4 o = acc[i];
-      o.x += ga * s0.x;
-      o.y += ga * s0.y;
-      o.z += ga * s0.z;
-      o.w += ga * s0.w;
-      *reinterpret_cast<float4*>(dst + off) = o;
+      o.x += ga * s0[i].x;
+      o.y += ga * s0[i].y;
+      o.z += ga * s0[i].z;
+      o.w += ga * s0[i].w;
+      *reinterpret_cast<float4*>(dst + (size_t)(vb * kRows + r) * Dk + d) = o;
     }
   }
 }
@@ -153,7 +178,7 @@ hipError_t launch_commit(const gdn_tree_commit_args& c, unsigned long long* err,
   a.n_seq = c.dims.n_seq;
   hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, s, err);
   if (c.n_path > 0) {
-    dim3 grid(c.n_path, c.dims.H, c.dims.Dv / kRows);
+    dim3 grid(c.n_path, c.dims.H, (c.dims.Dv + kRows - 1) / kRows);
     if (c.dims.dtype == GDN_BF16) hipLaunchKernelGGL(k_commit<__bf16>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_commit<float>, grid, dim3(256), 0, s, a);
   }
