@@ -24,11 +24,15 @@ def _compare(parent, seq_start, **kw):
     for f in ["seg_start", "seg_len", "seg_seq", "seg_mode", "seg_entry", "seg_slot", "seg_level"]:
         assert np.array_equal(got[f], ref[f]), f
     assert np.array_equal(got["tree_mask"], ref["tree_mask"])
-    # levels: the set of segments of every level (order inside a level is unspecified)
+    # levels: the set of segments of every level, listed longest first by chunk
+    # count (counts of 63 and more tie; order among ties is unspecified)
     ptr = got["level_ptr"]
+    nch = np.where(ref["seg_mode"] == 1, 1, (ref["seg_len"] + 63) // 64)
     for lv in range(len(got["level_count"])):
-        items = sorted(got["level_items"][ptr[lv]:ptr[lv + 1]].tolist())
-        assert items == np.nonzero(ref["seg_level"] == lv)[0].tolist()
+        lst = got["level_items"][ptr[lv]:ptr[lv + 1]]
+        assert sorted(lst.tolist()) == np.nonzero(ref["seg_level"] == lv)[0].tolist()
+        key = np.minimum(nch[lst], 63)
+        assert np.all(key[:-1] >= key[1:]), (lv, key.tolist())
     return got, ref
 
 

@@ -44,8 +44,9 @@ struct Meta {
   int* out_map;
   int* state_map;
   int* seg_depth0;
-  int* level_fill;
-  int* walk_ctr;
+  int* level_fill;  // [max_levels][kLenBuckets] entries placed so far
+  int* level_bkt;   // [max_levels][kLenBuckets] segments per length bucket
+  int* walk_ctr;    // [max_levels][kSchedInts]: the walk's work counters, then fewest and most chunks of a segment
   int* scan_sums;  // [2 * n_scan_blocks] block totals, then their exclusive offsets
   unsigned long long* plan_tag;  // fingerprint of the sizes the metadata was built for
   int4* unit_info;  // per level entry (level_items order): {start, len, mode | seq << 1, fork slot}
@@ -53,10 +54,16 @@ struct Meta {
 
 constexpr int kScanTile = 4096;  // tokens per block of the metadata scans
 constexpr int kWalkQueues = 8;  // work counters per level: one per XCD of the walk's grid
+constexpr int kSchedInts = kWalkQueues + 2;  // per level: the counters, the fewest and the most chunks of a segment
+// Each level lists its segments longest first, by chunk count (bucket 0: 63 or
+// more chunks, bucket 63 - c: c chunks), so that the walk's queues start the
+// longest items first.
+constexpr int kLenBuckets = 64;
+__host__ __device__ inline int len_bucket(int nchunks) { return kLenBuckets - 1 - (nchunks < kLenBuckets - 1 ? nchunks : kLenBuckets - 1); }
 
 struct LayoutFull {
   gdn_tree_layout pub;
-  size_t is_start, is_fork, out_map, state_map, seg_depth0, level_fill, walk_ctr, scan_sums, plan_tag, unit_info;
+  size_t is_start, is_fork, out_map, state_map, seg_depth0, level_fill, level_bkt, walk_ctr, scan_sums, plan_tag, unit_info;
   int n_scan_blocks;
 };
 

@@ -57,11 +57,12 @@ __global__ void k_init(Meta m, int T, int n_seq, int max_levels) {
     m.depth[i] = 0;
   }
   if (i < (long long)n_seq * kChunk) m.tree_mask[i] = 0ull;
-  if (i < max_levels) {
-    m.level_count[i] = 0;
+  if (i < max_levels) m.level_count[i] = 0;
+  if (i < (long long)max_levels * kLenBuckets) {
     m.level_fill[i] = 0;
+    m.level_bkt[i] = 0;
   }
-  if (i < (long long)max_levels * kWalkQueues) m.walk_ctr[i] = 0;
+  if (i < (long long)max_levels * kSchedInts) m.walk_ctr[i] = (i % kSchedInts) == kWalkQueues ? 0x7fffffff : 0;
   if (i == 0) {
     *m.err = kNoError;
     *m.n_seg = 0;
@@ -71,7 +72,8 @@ __global__ void k_init(Meta m, int T, int n_seq, int max_levels) {
 }
 
 __global__ void k_replan_check(Meta m, int max_levels, unsigned long long tag) {
-  for (int i = threadIdx.x; i < max_levels * kWalkQueues; i += blockDim.x) m.walk_ctr[i] = 0;
+  for (int i = threadIdx.x; i < max_levels * kWalkQueues; i += blockDim.x)
+    m.walk_ctr[(i / kWalkQueues) * kSchedInts + i % kWalkQueues] = 0;
   if (threadIdx.x == 0 && *m.plan_tag != tag) raise_error(m.err, GDN_DEV_NOT_PLANNED, 0);
 }
 
@@ -291,7 +293,13 @@ __global__ void k_levels(int max_levels, Meta m) {
   }
   m.seg_level[i] = lv;
   m.seg_depth0[i] = d;
-  if (lv < max_levels) atomicAdd(&m.level_count[lv], 1);
+  if (lv < max_levels) {
+    atomicAdd(&m.level_count[lv], 1);
+    const int nch = m.seg_mode[i] ? 1 : (m.seg_len[i] + kChunk - 1) / kChunk;
+    atomicAdd(&m.level_bkt[lv * kLenBuckets + len_bucket(nch)], 1);
+    atomicMin(&m.walk_ctr[lv * kSchedInts + kWalkQueues], nch);
+    atomicMax(&m.walk_ctr[lv * kSchedInts + kWalkQueues + 1], nch);
+  }
 }
 
 // Last launch of a plan. Blocks [0, gT) fill the level lists (thread i takes
@@ -324,9 +332,15 @@ __global__ void __launch_bounds__(256) k_finish(const int* parent, const int* se
     if (i < *m.n_seg) {
       const int lv = m.seg_level[i];
       if (lv < max_levels) {
-        const int pos = atomicAdd(&m.level_fill[lv], 1);
-        m.level_items[lptr[lv] + pos] = i;
-        m.unit_info[lptr[lv] + pos] = make_int4(m.seg_start[i], m.seg_len[i], m.seg_mode[i] | (m.seg_seq[i] << 1),
+        // longest first: the entries of longer buckets of the level come before
+        const int nch = m.seg_mode[i] ? 1 : (m.seg_len[i] + kChunk - 1) / kChunk;
+        const int bk = len_bucket(nch);
+        const int* cnt = m.level_bkt + lv * kLenBuckets;
+        int pos = lptr[lv];
+        for (int b = 0; b < bk; ++b) pos += cnt[b];
+        pos += atomicAdd(&m.level_fill[lv * kLenBuckets + bk], 1);
+        m.level_items[pos] = i;
+        m.unit_info[pos] = make_int4(m.seg_start[i], m.seg_len[i], m.seg_mode[i] | (m.seg_seq[i] << 1),
                                                 m.seg_slot[i]);
       }
     }
@@ -402,8 +416,9 @@ bool compute_layout(const gdn_tree_dims& d, LayoutFull* L) {
   L->out_map = take(4 * T);
   L->state_map = take(4 * T);
   L->seg_depth0 = take(4 * T);
-  L->level_fill = take(4 * (size_t)d.max_levels);
-  L->walk_ctr = take(4 * (size_t)d.max_levels * kWalkQueues);
+  L->level_fill = take(4 * (size_t)d.max_levels * kLenBuckets);
+  L->level_bkt = take(4 * (size_t)d.max_levels * kLenBuckets);
+  L->walk_ctr = take(4 * (size_t)d.max_levels * kSchedInts);
   L->n_scan_blocks = (int)((T + kScanTile - 1) / kScanTile);
   if (L->n_scan_blocks < 1) L->n_scan_blocks = 1;
   L->scan_sums = take(4 * 4 * (size_t)L->n_scan_blocks);
@@ -443,6 +458,7 @@ Meta meta_from(void* ws, const LayoutFull& L) {
   m.state_map = (int*)(b + L.state_map);
   m.seg_depth0 = (int*)(b + L.seg_depth0);
   m.level_fill = (int*)(b + L.level_fill);
+  m.level_bkt = (int*)(b + L.level_bkt);
   m.walk_ctr = (int*)(b + L.walk_ctr);
   m.scan_sums = (int*)(b + L.scan_sums);
   m.plan_tag = (unsigned long long*)(b + L.plan_tag);
@@ -475,7 +491,8 @@ hipError_t launch_plan(const gdn_tree_fwd_args& a, const Meta& m, const LayoutFu
   const int bs = 256;
   long long init_n = T;
   if ((long long)n_seq * kChunk > init_n) init_n = (long long)n_seq * kChunk;
-  if ((long long)ml * kWalkQueues > init_n) init_n = (long long)ml * kWalkQueues;
+  if ((long long)ml * kSchedInts > init_n) init_n = (long long)ml * kSchedInts;
+  if ((long long)ml * kLenBuckets > init_n) init_n = (long long)ml * kLenBuckets;
   if (init_n < 1) init_n = 1;
   const int gT = blocks_for(T > 0 ? T : 1, bs);
   const int* out_rows = a.n_out > 0 ? a.out_rows : nullptr;

@@ -193,7 +193,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_walk(WalkArgs a) {
 
   for (;;) {
     __syncthreads();
-    if (tid == 0) *sItem = atomicAdd(&m.walk_ctr[lvl], 1);
+    if (tid == 0) *sItem = atomicAdd(&m.walk_ctr[lvl * kSchedInts], 1);
     __syncthreads();
     const long long item = *sItem;
     if (item >= total) break;

@@ -138,6 +138,7 @@ struct Args {
   const unsigned long long* err;
   const int* level_count;
   const int* level_ptr;
+  int* walk_ctr;  // per level: items claimed so far per XCD (zeroed by the plan), fewest and most chunks of an item
   int H, Dv, NT, level, out_all;
 };
 
@@ -199,71 +200,139 @@ __device__ __forceinline__ T lds_at(const unsigned char* base, int byte_off) {
 __device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // --------------------------------------------------------------- item feed
-// The second helper walks the level's items in a fixed order: the workgroups
-// of one XCD share the units (segment, head) whose index is congruent to the
-// XCD mod 8, so all d_v tiles of a unit read its q and k through the same L2,
-// and the k-th workgroup of the XCD takes the XCD's items k, k + G, k + 2 G,
-// ... (G workgroups per XCD). The unit record of the next item is loaded
-// while the current one is walked.
+// The workgroups of one XCD share the units (segment, head) whose index is
+// congruent to the XCD mod 8, so all d_v tiles of a unit read its q and k
+// through the same L2. The k-th workgroup of an XCD starts with the XCD's item
+// k. After that, in a level whose items all have the same chunk count, it takes
+// items k + G, k + 2 G, ... (G workgroups per XCD); in any other level it claims
+// its next item from the XCD's counter, only shortly before it needs it: the
+// level lists segments longest first, so long and short items balance like a
+// longest-first list schedule, and claims are spread out in time (contended
+// claims on one counter are slow). A claim takes two feed calls to become
+// usable (the index arrives, then the unit record it names), so the next item
+// is claimed when one chunk of the current item is left to feed, and the one
+// after it as well when the current item is short (items of one or two chunks
+// then follow each other without a stall). Only the first of the two waiting
+// items has its unit record requested, which keeps one record and one index in
+// flight.
 
 struct Feed {
-  int start, len, mode, sq, slot, h, tile, nch, c;
-  bool cur;     // an item is being walked
-  int li;       // XCD-local index of the next item to start
-  int4 info_v;  // unit record of that item (in flight until the next vmcnt(0))
-  bool nx_valid;
+  int start, len, ms, slot;  // unit record of the current item: first token, length, mode | sequence << 1, fork slot
+  int h, tile, nch, c;       // its head, d_v tile, chunks, chunks fed so far
+  int u0, tile0;             // unit and d_v tile of the first waiting item once its index is known
+  int nst;                   // items taken so far in the fixed stride
+  int fl;                    // kFeedDone | kFeedDyn | stage of the first waiting item | kFeedWait1
+};
+// Stages of the first waiting item (bits 0-1 of fl): none, index in flight,
+// index known and unit record requested.
+constexpr int kFeedIdx = 1, kFeedRec = 2, kFeedStage = 3;
+constexpr int kFeedWait1 = 4;  // a second item is waiting (its index in flight)
+constexpr int kFeedDyn = 8;    // items are claimed from the counter (else taken in a fixed stride)
+constexpr int kFeedDone = 16;  // the level has no item left for this workgroup
+
+struct FeedRegs {
+  int raw0, raw1;  // indices of the waiting items in lane 0 (a claim is in flight until the next vmcnt(0))
+  int4 info0;      // unit record of the first waiting item (likewise)
 };
 
-// Unit indices stay below count * H <= T * H < 2^31 (checked on the host).
-__device__ __forceinline__ void feed_prefetch(Feed& f, const Args& a, int xcd, int count, int base) {
-  const unsigned u = (unsigned)xcd + (unsigned)kXcd * ((unsigned)f.li / (unsigned)a.NT);
-  f.nx_valid = u < (unsigned)count * (unsigned)a.H;
-  f.info_v = make_int4(0, 0, 0, -1);
-  if (f.nx_valid) f.info_v = a.unit_info[base + (int)(u / (unsigned)a.H)];
+// Index of the workgroup's next item after its first.
+__device__ __forceinline__ int feed_claim(Feed& f, const Args& a, int xcd, int lane) {
+  const int G = (int)(gridDim.x / kXcd);
+  if (!(f.fl & kFeedDyn)) return (int)(blockIdx.x / kXcd) + G * ++f.nst;
+  int v = 0;
+  if (lane == 0) v = atomicAdd(a.walk_ctr + a.level * kSchedInts + xcd, 1) + G;
+  return v;
+}
+
+// First waiting item, index -> record: reads its index and requests its unit
+// record. Unit indices stay below count * H <= T * H < 2^31 (checked on the
+// host); a unit past the level's last one ends the level.
+__device__ __forceinline__ void feed_advance(Feed& f, FeedRegs& r, const Args& a, int xcd, int count, int base) {
+  if ((f.fl & kFeedStage) != kFeedIdx) return;
+  const unsigned idx = (unsigned)rfl(r.raw0);
+  const unsigned q = idx / (unsigned)a.NT;
+  const unsigned u = (unsigned)xcd + (unsigned)kXcd * q;
+  f.u0 = (int)u;
+  f.tile0 = (int)(idx - q * (unsigned)a.NT);
+  r.info0 = make_int4(0, 0, 0, -1);
+  if (u < (unsigned)count * (unsigned)a.H) r.info0 = a.unit_info[base + (int)(u / (unsigned)a.H)];
+  f.fl += kFeedRec - kFeedIdx;
+}
+
+// The workgroup's first item waits with its index known (its rank among the
+// XCD's workgroups).
+__device__ __forceinline__ void feed_init(Feed& f, FeedRegs& r, const Args& a) {
+  f = Feed{};
+  const int* sc = a.walk_ctr + a.level * kSchedInts + kWalkQueues;
+  f.fl = kFeedIdx | (sc[0] != sc[1] ? kFeedDyn : 0);
+  r.raw0 = (int)(blockIdx.x / kXcd);
+  r.raw1 = 0;
+  r.info0 = make_int4(0, 0, 0, -1);
 }
 
 // The descriptor of the next chunk to load (valid = 0 when the level is done).
-// Reads the prefetched unit record: call it only after a vmcnt(0).
+// Called once per helper iteration, after its vmcnt(0), so that what the
+// previous call requested has arrived.
 template <int BV>
-__device__ __forceinline__ Desc feed_next(Feed& f, const Args& a, int xcd, int count, int base, int per_xcd) {
+__device__ __forceinline__ Desc feed_next(Feed& f, FeedRegs& r, const Args& a, int xcd, int count, int base,
+                                          int lane) {
   Desc d = {};  // every field defined, also when the level is done
-  if (!(f.cur && f.c < f.nch)) {
-    f.cur = false;
-    if (!f.nx_valid) return d;
-    const unsigned u = (unsigned)xcd + (unsigned)kXcd * ((unsigned)f.li / (unsigned)a.NT);
-    f.start = rfl(f.info_v.x);
-    f.len = rfl(f.info_v.y);
-    const int ms = rfl(f.info_v.z);
-    f.mode = ms & 1;
-    f.sq = ms >> 1;
-    f.slot = rfl(f.info_v.w);
+  if (f.fl & kFeedDone) return d;
+  const bool sw = f.c >= f.nch;  // the current item is over (or none has started)
+  if (sw && !(f.fl & kFeedStage)) {  // nothing waiting: claim now (the advance below waits for it)
+    r.raw0 = feed_claim(f, a, xcd, lane);
+    f.fl |= kFeedIdx;
+  }
+  feed_advance(f, r, a, xcd, count, base);
+  if (sw) {
+    const unsigned u = (unsigned)f.u0;
+    if (u >= (unsigned)count * (unsigned)a.H) {  // claims run past the level's items
+      f.fl |= kFeedDone;
+      return d;
+    }
+    f.start = rfl(r.info0.x);
+    f.len = rfl(r.info0.y);
+    f.ms = rfl(r.info0.z);
+    f.slot = rfl(r.info0.w);
     f.h = (int)(u % (unsigned)a.H);
-    f.tile = (int)((unsigned)f.li % (unsigned)a.NT);
-    f.nch = f.mode ? 1 : (f.len + kChunk - 1) / kChunk;
+    f.tile = f.tile0;
+    f.nch = (f.ms & 1) ? 1 : (f.len + kChunk - 1) / kChunk;
     f.c = 0;
-    f.cur = true;
-    f.li += per_xcd;
-    feed_prefetch(f, a, xcd, count, base);
+    // the second waiting item moves up; its claim was made in an earlier call
+    f.fl = (f.fl & ~(kFeedStage | kFeedWait1)) | ((f.fl & kFeedWait1) ? kFeedIdx : 0);
+    r.raw0 = r.raw1;
+    feed_advance(f, r, a, xcd, count, base);
   }
   const size_t SS = (size_t)a.Dv * DK;
+  const int mode = f.ms & 1, sq = f.ms >> 1;
   d.valid = 1;
   d.t0 = f.start + f.c * kChunk;
   d.n = min(kChunk, f.len - f.c * kChunk);
   d.h = f.h;
   d.v0 = f.tile * BV;
-  d.mode = f.mode;
-  d.sq = f.sq;
+  d.mode = mode;
+  d.sq = sq;
   d.first = f.c == 0;
-  d.need_exit = (!f.mode) && (f.c + 1 < f.nch);
+  d.need_exit = (!mode) && (f.c + 1 < f.nch);
   d.has_out = 0;
   d.req_lo = d.req_hi = 0;
   d.sin = nullptr;
   if (d.first) {
     const float* s = f.slot >= 0 ? a.fork_states + ((size_t)f.slot * a.H + f.h) * SS
-                                 : (a.init ? a.init + ((size_t)f.sq * a.H + f.h) * SS : nullptr);
+                                 : (a.init ? a.init + ((size_t)sq * a.H + f.h) * SS : nullptr);
     d.sin = s ? s + (size_t)d.v0 * DK : nullptr;
   }
   f.c += 1;
+  const int rem = f.nch - f.c;
+  const int need = rem == 0 ? (f.nch <= 2 ? 2 : 1) : (rem == 1 ? 1 : 0);
+  if (need >= 1 && !(f.fl & kFeedStage)) {
+    r.raw0 = feed_claim(f, a, xcd, lane);
+    f.fl |= kFeedIdx;
+  }
+  if (need >= 2 && !(f.fl & kFeedWait1)) {
+    r.raw1 = feed_claim(f, a, xcd, lane);
+    f.fl |= kFeedWait1;
+  }
   return d;
 }
 
@@ -573,8 +642,8 @@ __device__ __forceinline__ void chunk_products(int hid, const Desc& c, const uns
 }
 
 template <int BV>
-__device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, int hid, int lane, Feed& f, int xcd, int count,
-                            int base, int per_xcd) {
+__device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, int hid, int lane, Feed& ff, FeedRegs& fr, int xcd,
+                                            int count, int base) {
   using C = Cfg<BV>;
   Desc* nds = reinterpret_cast<Desc*>(smem + C::oND);
   float* lt = reinterpret_cast<float*>(smem + C::oLT);
@@ -596,7 +665,7 @@ __device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, 
     if (hid == 1) {
       store_tokens(a, nd, tr, smem + C::oTB + s2 * kTB, lane);
       Desc nn = {};
-      if (nd.valid) nn = feed_next<BV>(f, a, xcd, count, base, per_xcd);
+      if (nd.valid) nn = feed_next<BV>(ff, fr, a, xcd, count, base, lane);
       put_desc(reinterpret_cast<unsigned char*>(nds + ((it + 1) & 1)), nn, lane);
     }
     lds_barrier();
@@ -953,7 +1022,6 @@ __global__ void __launch_bounds__(Cfg<BV>::NTHR, 1) k_walk_pipe(const Args a) {
   const int count = a.level_count[a.level];
   const int base = a.level_ptr[a.level];
   const int xcd = blockIdx.x % kXcd;
-  const int per_xcd = gridDim.x / kXcd;
   const bool helper = w >= C::NS;
   const int hid = w - C::NS;  // 0 or 1 on the helpers
 
@@ -967,16 +1035,15 @@ __global__ void __launch_bounds__(Cfg<BV>::NTHR, 1) k_walk_pipe(const Args a) {
   // ---- prologue: describe chunks 0 and 1 and copy K, Q and the token tables
   // of chunk 0; the helpers' first loop iteration forms its products
   Desc* nds = reinterpret_cast<Desc*>(smem + C::oND);
-  Feed f;
-  f.cur = false;
-  f.li = blockIdx.x / kXcd;
-  f.nx_valid = false;
+  Feed ff;
+  FeedRegs fr;
+  feed_init(ff, fr, a);
   if (hid == 1) {
-    feed_prefetch(f, a, xcd, count, base);
-    wait_vm();
-    put_desc(reinterpret_cast<unsigned char*>(nds + 0), feed_next<BV>(f, a, xcd, count, base, per_xcd), lane);
-    wait_vm();
-    put_desc(reinterpret_cast<unsigned char*>(nds + 1), feed_next<BV>(f, a, xcd, count, base, per_xcd), lane);
+#pragma nounroll
+    for (int i = 0; i < 2; ++i) {
+      put_desc(reinterpret_cast<unsigned char*>(nds + i), feed_next<BV>(ff, fr, a, xcd, count, base, lane), lane);
+      wait_vm();
+    }
   }
   lds_barrier();
   if (helper) {
@@ -989,7 +1056,7 @@ __global__ void __launch_bounds__(Cfg<BV>::NTHR, 1) k_walk_pipe(const Args a) {
   }
   lds_barrier();
 
-  if (helper) helper_loop<BV>(a, smem, hid, lane, f, xcd, count, base, per_xcd);
+  if (helper) helper_loop<BV>(a, smem, hid, lane, ff, fr, xcd, count, base);
   else state_loop<BV>(a, smem, w, lane);
 }
 
@@ -1049,6 +1116,7 @@ hipError_t launch_walk_pipe(const gdn_tree_fwd_args& fa, const Meta& m, int bv, 
   wa.err = m.err;
   wa.level_count = m.level_count;
   wa.level_ptr = m.level_ptr;
+  wa.walk_ctr = m.walk_ctr;
   wa.H = fa.dims.H;
   wa.Dv = fa.dims.Dv;
   wa.NT = fa.dims.Dv / bv;
