@@ -52,7 +52,7 @@ struct Meta {
   int4* unit_info;  // per level entry (level_items order): {start, len, mode | seq << 1, fork slot}
 };
 
-constexpr int kScanTile = 4096;  // tokens per block of the metadata scans
+constexpr int kScanTile = 1024;  // tokens per block of the metadata scans (four per thread)
 constexpr int kWalkQueues = 8;  // work counters per level: one per XCD of the walk's grid
 constexpr int kSchedInts = kWalkQueues + 2;  // per level: the counters, the fewest and the most chunks of a segment
 // Each level lists its segments longest first, by chunk count (bucket 0: 63 or

@@ -236,66 +236,86 @@ __global__ void __launch_bounds__(256) k_scan_apply(int T, int nb, int max_forks
     base_a = m.scan_sums[2 * nb + 2 * blockIdx.x];
     base_f = m.scan_sums[2 * nb + 2 * blockIdx.x + 1];
   }
-  int base = blockIdx.x * kScanTile + threadIdx.x * per;
-  int a = 0, f = 0;
-  for (int i = 0; i < per; ++i) {
-    int t = base + i;
-    if (t < T) { a += m.is_start[t]; f += m.is_fork[t]; }
+  static_assert(per == 4, "one int4 of each flag array per thread");
+  const int base = blockIdx.x * kScanTile + threadIdx.x * per;
+  int st[4] = {0, 0, 0, 0}, fk[4] = {0, 0, 0, 0};
+  if (base + 4 <= T) {  // the tables are 16-byte aligned
+    const int4 vs = *reinterpret_cast<const int4*>(m.is_start + base);
+    const int4 vf = *reinterpret_cast<const int4*>(m.is_fork + base);
+    st[0] = vs.x, st[1] = vs.y, st[2] = vs.z, st[3] = vs.w;
+    fk[0] = vf.x, fk[1] = vf.y, fk[2] = vf.z, fk[3] = vf.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < per; ++i)
+      if (base + i < T) {
+        st[i] = m.is_start[base + i];
+        fk[i] = m.is_fork[base + i];
+      }
   }
+  const int a = st[0] + st[1] + st[2] + st[3], f = fk[0] + fk[1] + fk[2] + fk[3];
   int ta, tf;
   int ea = block_excl_scan(a, sh, &ta) + base_a;
   int ef = block_excl_scan(f, sh, &tf) + base_f;
+#pragma unroll
   for (int i = 0; i < per; ++i) {
-    int t = base + i;
-    if (t >= T) break;
-    if (m.is_start[t]) m.seg_start[ea++] = t;
-    if (m.is_fork[t]) {
+    const int t = base + i;
+    if (st[i]) m.seg_start[ea++] = t;
+    if (fk[i]) {
       if (ef == max_forks) raise_error(m.err, GDN_DEV_FORK_CAPACITY, t);
       m.fork_slot[t] = ef++;
     }
   }
 }
 
-__global__ void k_segments(const int* parent, const int* seq_start, int T, Meta m) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  int n_seg = *m.n_seg;
-  if (i >= n_seg || bad_csr(m)) return;
-  int start = m.seg_start[i];
-  int end = (i + 1 < n_seg) ? m.seg_start[i + 1] : T;
-  int s = m.tok_seq[start];
-  int mode = (seq_start[s + 1] - seq_start[s]) <= kChunk ? 1 : 0;
-  int e = mode ? -1 : parent[start];
-  if (e < 0 || e >= start) e = -1;  // invalid parents were reported; never follow them
-  m.seg_len[i] = end - start;
-  m.seg_seq[i] = s;
-  m.seg_mode[i] = mode;
-  m.seg_entry[i] = e;
-  m.seg_slot[i] = (e >= 0) ? m.fork_slot[e] : -1;
+// Entry token of segment j (the parent of its first token), or -1 when it
+// starts from an initial state: a tree chunk always does, and invalid parents
+// (already reported) are never followed.
+__device__ inline int seg_entry_of(const int* parent, const int* seq_start, const Meta& m, int start, int* seq,
+                                   int* mode) {
+  const int s = m.tok_seq[start];
+  const int md = (seq_start[s + 1] - seq_start[s]) <= kChunk ? 1 : 0;
+  int e = md ? -1 : parent[start];
+  if (e < 0 || e >= start) e = -1;
+  *seq = s;
+  *mode = md;
+  return e;
 }
 
-__global__ void k_levels(int max_levels, Meta m) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  int n_seg = *m.n_seg;
-  if (i >= n_seg) return;
-  int lv = 0, d = 0, cur = i;
-  for (;;) {
-    int e = m.seg_entry[cur];
-    if (e < 0) break;
+// Thread i takes segment i: its table row, then its dependency level (the
+// number of forks on the way to an initial state, each hop found by a binary
+// search of the segment starts) and the level's counts.
+__global__ void k_seglev(const int* parent, const int* seq_start, int T, int max_levels, Meta m) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int n_seg = *m.n_seg;
+  if (i >= n_seg || bad_csr(m)) return;
+  const int start = m.seg_start[i];
+  const int end = (i + 1 < n_seg) ? m.seg_start[i + 1] : T;
+  int sq, mode;
+  const int e0 = seg_entry_of(parent, seq_start, m, start, &sq, &mode);
+  m.seg_len[i] = end - start;
+  m.seg_seq[i] = sq;
+  m.seg_mode[i] = mode;
+  m.seg_entry[i] = e0;
+  m.seg_slot[i] = (e0 >= 0) ? m.fork_slot[e0] : -1;
+  int lv = 0, d = 0, e = e0;
+  while (e >= 0) {
     if (lv + 1 >= max_levels) {
-      raise_error(m.err, GDN_DEV_LEVEL_CAPACITY, m.seg_start[i]);
+      raise_error(m.err, GDN_DEV_LEVEL_CAPACITY, start);
       lv = max_levels;
       break;
     }
     ++lv;
-    int j = seg_of(m.seg_start, n_seg, e);
-    d += e - m.seg_start[j] + 1;
-    cur = j;
+    const int j = seg_of(m.seg_start, n_seg, e);
+    const int sj = m.seg_start[j];
+    d += e - sj + 1;
+    int sq_j, mode_j;
+    e = seg_entry_of(parent, seq_start, m, sj, &sq_j, &mode_j);
   }
   m.seg_level[i] = lv;
   m.seg_depth0[i] = d;
   if (lv < max_levels) {
     atomicAdd(&m.level_count[lv], 1);
-    const int nch = m.seg_mode[i] ? 1 : (m.seg_len[i] + kChunk - 1) / kChunk;
+    const int nch = mode ? 1 : (end - start + kChunk - 1) / kChunk;
     atomicAdd(&m.level_bkt[lv * kLenBuckets + len_bucket(nch)], 1);
     atomicMin(&m.walk_ctr[lv * kSchedInts + kWalkQueues], nch);
     atomicMax(&m.walk_ctr[lv * kSchedInts + kWalkQueues + 1], nch);
@@ -517,8 +537,7 @@ hipError_t launch_plan(const gdn_tree_fwd_args& a, const Meta& m, const LayoutFu
       hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(256), 0, s, nb, m);
       hipLaunchKernelGGL(k_scan_apply<false>, dim3(nb), dim3(256), 0, s, T, nb, a.dims.max_forks, m);
     }
-    hipLaunchKernelGGL(k_segments, dim3(gT), dim3(bs), 0, s, a.parent_idx, a.seq_start, T, m);
-    hipLaunchKernelGGL(k_levels, dim3(gT), dim3(bs), 0, s, ml, m);
+    hipLaunchKernelGGL(k_seglev, dim3(gT), dim3(bs), 0, s, a.parent_idx, a.seq_start, T, ml, m);
   }
   const int tree_blocks = work ? blocks_for(n_seq, 4) : 0;
   hipLaunchKernelGGL(k_finish, dim3(gT + tree_blocks), dim3(bs), 4 * (ml + 1), s, a.parent_idx, a.seq_start, T, n_seq,
