@@ -336,6 +336,29 @@ __device__ __forceinline__ Desc feed_next(Feed& f, FeedRegs& r, const Args& a, i
   return d;
 }
 
+// The fields of a descriptor the state waves use, wave-uniform.
+struct SDesc {
+  int valid, t0, n, h, v0, mode, has_out, need_exit, first;
+  unsigned req_lo, req_hi;
+};
+
+__device__ __forceinline__ SDesc load_sdesc(const unsigned char* p) {
+  const Desc* dp = reinterpret_cast<const Desc*>(p);
+  SDesc d;
+  d.valid = rfl(dp->valid);
+  d.t0 = rfl(dp->t0);
+  d.n = rfl(dp->n);
+  d.h = rfl(dp->h);
+  d.v0 = rfl(dp->v0);
+  d.mode = rfl(dp->mode);
+  d.has_out = rfl(dp->has_out);
+  d.need_exit = rfl(dp->need_exit);
+  d.first = rfl(dp->first);
+  d.req_lo = (unsigned)rfl((int)dp->req_lo);
+  d.req_hi = (unsigned)rfl((int)dp->req_hi);
+  return d;
+}
+
 // A descriptor read from LDS, with every field made wave-uniform.
 __device__ __forceinline__ Desc uniform_desc(const Desc& s) {
   Desc d;
@@ -682,6 +705,54 @@ struct SOff {
   int V[NB];   // transposed read of V rows 4 g4 + l16/4, column block nb (row block rb adds 32 BV rb)
 };
 
+// dst = cS src + (K^T rows of the state block) x (decayed pseudo-values w) for
+// every 16-column block and d_k tile; dst may be src (each tile depends only on
+// its own tile of src).
+template <int NB>
+__device__ __forceinline__ void state_at(f32x4 (&dst)[NB][8], const f32x4 (&src)[NB][8], float cS, const unsigned char* kq,
+                                         const SOff<NB>& o, const bf16x8 (&w01)[NB], const bf16x8 (&w23)[NB]) {
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    // A operand: K^T rows (d_k) of this state block against tokens 0..31 and 32..63
+    const unsigned char* kp = kq + o.KT[dt];
+    const bf16x8 k01 = cat8(tr_read(kp), tr_read(kp + 4096));
+    const bf16x8 k23 = cat8(tr_read(kp + 8192), tr_read(kp + 8192 + 4096));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4 t;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) t[r] = cS * src[nb][dt][r];
+      t = mma32(k01, w01[nb], t);
+      dst[nb][dt] = mma32(k23, w23[nb], t);
+    }
+  }
+}
+
+// A state after a requested token to its fork slot and/or state row.
+template <int NB>
+__device__ __forceinline__ void store_state(const Args& a, const f32x4 (&S)[NB][8], int fs, int sr, int h, int v0w,
+                                            int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const size_t SS = (size_t)a.Dv * DK;
+  const size_t roff = (size_t)(v0w + l16) * DK + 8 * g4;
+  if (fs >= 0) {
+    float* dst = a.fork_states + ((size_t)fs * a.H + h) * SS + roff;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4*>(dst + 16 * nb * DK + 32 * (dt >> 1) + 4 * (dt & 1)) = S[nb][dt];
+  }
+  if (sr >= 0) {
+    float* dst = a.state_out + ((size_t)sr * a.H + h) * SS + roff;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4*>(dst + 16 * nb * DK + 32 * (dt >> 1) + 4 * (dt & 1)) = S[nb][dt];
+  }
+}
+
 // One chunk on a state wave: K S_e^T, R, the block substitution, the outputs
 // and pseudo-values, then the states after requested tokens and at the exit.
 // The wave owns NB blocks of 16 columns. ST[nb][dt] (dt = 2 m + bb) holds S^T
@@ -830,7 +901,6 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
   // states after requested tokens (fork slots, state rows) and at the chunk exit
   if (!todo) return;
   const float* sG2 = reinterpret_cast<const float*>(tb + tG2);
-  const size_t SS = (size_t)a.Dv * DK;
   do {
     const int p = __builtin_ctzll(todo);
     todo &= todo - 1ull;
@@ -880,48 +950,20 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
       w23[nb] = cat8b(Wb[2], Wb[3]);
     }
     const float cS = sEG[p];
-    f32x4 acc[NB][8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      // A operand: K^T rows (d_k) of this state block against tokens 0..31 and 32..63
-      const unsigned char* kp = kq + o.KT[dt];
-      const bf16x8 k01 = cat8(tr_read(kp), tr_read(kp + 4096));
-      const bf16x8 k23 = cat8(tr_read(kp + 8192), tr_read(kp + 8192 + 4096));
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[nb][dt][r] = cS * ST[nb][dt][r];
-        acc[nb][dt] = mma32(k01, w01[nb], acc[nb][dt]);
-        acc[nb][dt] = mma32(k23, w23[nb], acc[nb][dt]);
-      }
-    }
     const int fs = reinterpret_cast<const int*>(tb + tFS)[p];
     const int sr = reinterpret_cast<const int*>(tb + tSR)[p];
-    const size_t roff = (size_t)(v0w + l16) * DK + 8 * g4;
-    if (fs >= 0) {
-      float* dst = a.fork_states + ((size_t)fs * a.H + h) * SS + roff;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          *reinterpret_cast<f32x4*>(dst + 16 * nb * DK + 32 * (dt >> 1) + 4 * (dt & 1)) = acc[nb][dt];
-    }
-    if (sr >= 0) {
-      float* dst = a.state_out + ((size_t)sr * a.H + h) * SS + roff;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          *reinterpret_cast<f32x4*>(dst + 16 * nb * DK + 32 * (dt >> 1) + 4 * (dt & 1)) = acc[nb][dt];
-    }
     if (need_exit && p == n - 1) {
+      // the chunk exit (always the last requested token): S is updated in place
+      state_at<NB>(ST, ST, cS, kq, o, w01, w23);
+      store_state<NB>(a, ST, fs, sr, h, v0w, lane);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) ST[nb][dt] = acc[nb][dt];
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int m = 0; m < 4; ++m) Sb[nb][m] = cat8b(to_bf4(ST[nb][2 * m]), to_bf4(ST[nb][2 * m + 1]));
-      }
+    } else {
+      f32x4 acc[NB][8];
+      state_at<NB>(acc, ST, cS, kq, o, w01, w23);
+      store_state<NB>(a, acc, fs, sr, h, v0w, lane);
     }
   } while (todo);
 }
@@ -981,14 +1023,18 @@ __device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, i
   }
 
   lds_barrier();  // the helpers' iteration -1
+  // The descriptor of chunk it + 1 is complete during chunk it (the helpers
+  // wrote it one iteration earlier), so it is read before the barrier that
+  // ends chunk it and the next chunk starts without an LDS round trip.
+  SDesc cd = load_sdesc(smem + C::oTB + tD);
   for (int it = 0;; ++it) {
     const unsigned char* tb = smem + C::oTB + (it % 3) * kTB;
     const Desc* dp = reinterpret_cast<const Desc*>(tb + tD);
-    if (!rfl(dp->valid)) break;
-    const int t0 = rfl(dp->t0), n = rfl(dp->n), h = rfl(dp->h), v0 = rfl(dp->v0);
-    const int mode = rfl(dp->mode);
-    const bool has_out = rfl(dp->has_out), need_exit = rfl(dp->need_exit), first = rfl(dp->first);
-    unsigned long long todo = ((unsigned long long)(unsigned)rfl((int)dp->req_hi) << 32) | (unsigned)rfl((int)dp->req_lo);
+    if (!cd.valid) break;
+    const int t0 = cd.t0, n = cd.n, h = cd.h, v0 = cd.v0;
+    const int mode = cd.mode;
+    const bool has_out = cd.has_out, need_exit = cd.need_exit, first = cd.first;
+    unsigned long long todo = ((unsigned long long)cd.req_hi << 32) | cd.req_lo;
     if (need_exit) todo |= 1ull << (n - 1);
     const unsigned char* kq = smem + C::oKQ + (it % 3) * 32768;
     const unsigned char* vt = smem + C::oV + (it & 1) * C::VT;
@@ -1006,6 +1052,7 @@ __device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, i
       state_chunk<BV, true>(a, smem, tb, kq, vt, pr, o, ST, Sb, it, t0, n, h, v0w, mode, need_exit, todo, lane);
     else
       state_chunk<BV, false>(a, smem, tb, kq, vt, pr, o, ST, Sb, it, t0, n, h, v0w, mode, need_exit, todo, lane);
+    cd = load_sdesc(smem + C::oTB + ((it + 1) % 3) * kTB + tD);
     lds_barrier();
   }
 }
