@@ -68,12 +68,21 @@ def test_plan_full_size_structures():
 
 @pytest.mark.parametrize("case", ["order", "self", "below", "crossseq", "seqstart", "seqlast", "forkcap", "levelcap",
                                   "rowdup", "rowrange"])
-def test_plan_errors_match(case):
+@pytest.mark.parametrize("long", [False, True])
+def test_plan_errors_match(case, long):
+    """Short streams are planned by one workgroup, long ones by six launches:
+    both report the same first error as the reference planner."""
     wl = W.random_small(11, n_seq=4, H=1, Dk=16, Dv=16, max_len=200)
     parent = wl.parent.copy()
     seq = wl.seq_start.copy()
+    if long:  # a 5000-token chain appended as a fifth sequence
+        T0 = wl.T
+        chain = np.arange(T0 - 1, T0 + 4999, dtype=np.int32)
+        chain[0] = -1
+        parent = np.concatenate([parent, chain]).astype(np.int32)
+        seq = np.concatenate([seq, [T0 + 5000]]).astype(np.int32)
     kw = {}
-    T = wl.T
+    T = int(parent.shape[0])
     if case == "order":
         parent[T - 3] = T - 1
     elif case == "self":
@@ -97,7 +106,7 @@ def test_plan_errors_match(case):
         kw = {"out_rows": np.array([1, 2, 1], np.int32)}
     elif case == "rowrange":
         kw = {"state_rows": np.array([0, T], np.int32)}
-    say(f"plan error case {case}")
+    say(f"plan error case {case} long={long} T={T}")
     got, ref = _compare(parent, seq, **kw)
     if case not in ("forkcap", "levelcap") or ref["error"] != (0, 0):
         assert ref["error"] != (0, 0)

@@ -437,13 +437,15 @@ __device__ __forceinline__ void issue_v(const Args& a, const Desc& d, unsigned c
   }
 }
 
-// Helper 0 copies K and the first half of Q, helper 1 the rest of Q.
+// Helper 0 copies K and the first kQSplit blocks of 4 rows of Q, helper 1 the
+// rest of Q (helper 0 also inverts the diagonal blocks, so it takes fewer copies).
+constexpr int kQSplit = 4;
 __device__ __forceinline__ void issue_kq(const Args& a, const Desc& d, unsigned char* kq, int hid, int lane) {
   if (hid == 0) {
     issue_rows<0, 16>(a, d, a.k, kq, lane);
-    issue_rows<0, 8>(a, d, a.q, kq + 16384, lane);
+    issue_rows<0, kQSplit>(a, d, a.q, kq + 16384, lane);
   } else {
-    issue_rows<8, 16>(a, d, a.q, kq + 16384, lane);
+    issue_rows<kQSplit, 16>(a, d, a.q, kq + 16384, lane);
   }
 }
 
