@@ -13,6 +13,9 @@
 namespace gdn {
 namespace {
 
+// S_0 and S_a are streamed once: nontemporal loads and stores keep them from
+// displacing cached data (measured 15% faster on 64 paths x 32 heads).
+typedef float f32x4n __attribute__((ext_vector_type(4)));
 constexpr int kRows = 32;      // rows of S per workgroup
 constexpr int kPathTile = 16;  // path nodes staged in LDS at a time
 constexpr int kThreads = 256;
@@ -71,8 +74,9 @@ __global__ void __launch_bounds__(kThreads, 6) k_commit(CommitArgs a) {
   for (int i = 0; i < kPer4; ++i) {
     const int gidx = tid + kThreads * i;
     const int r = gidx / per_row4, d = (gidx % per_row4) * 4;
-    s0[i] = (S0 && gidx < n4 && r < rows) ? *reinterpret_cast<const float4*>(S0 + (size_t)(vb * kRows + r) * Dk + d)
-                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    f32x4n v = {0.f, 0.f, 0.f, 0.f};
+    if (S0 && gidx < n4 && r < rows) v = __builtin_nontemporal_load(reinterpret_cast<const f32x4n*>(S0 + (size_t)(vb * kRows + r) * Dk + d));
+    s0[i] = make_float4(v[0], v[1], v[2], v[3]);
   }
   const E* kg = reinterpret_cast<const E*>(a.k);
   const E* gg = reinterpret_cast<const E*>(a.g);
@@ -152,7 +156,8 @@ __global__ void __launch_bounds__(kThreads, 6) k_commit(CommitArgs a) {
       o.y += ga * s0[i].y;
       o.z += ga * s0[i].z;
       o.w += ga * s0[i].w;
-      *reinterpret_cast<float4*>(dst + (size_t)(vb * kRows + r) * Dk + d) = o;
+      f32x4n ov = {o.x, o.y, o.z, o.w};
+      __builtin_nontemporal_store(ov, reinterpret_cast<f32x4n*>(dst + (size_t)(vb * kRows + r) * Dk + d));
     }
   }
 }
