@@ -751,7 +751,7 @@ __device__ __forceinline__ void store_state(const Args& a, const f32x4 (&S)[NB][
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        __builtin_nontemporal_store(S[nb][dt], reinterpret_cast<f32x4*>(dst + 16 * nb * DK + 32 * (dt >> 1) + 4 * (dt & 1)));
+        *reinterpret_cast<f32x4*>(dst + 16 * nb * DK + 32 * (dt >> 1) + 4 * (dt & 1)) = S[nb][dt];
   }
 }
 
@@ -861,16 +861,14 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
         for (int nb = 0; nb < NB; ++nb) O[nb][rb] = mma32(cat8b(Vb[nb][2 * mp], Vb[nb][2 * mp + 1]), pb, O[nb][rb]);
       }
     }
-    // lane (l16, g4) holds columns 4 g4 .. 4 g4 + 3 of block nb for token 16 rb + l16;
-    // outputs and requested states are written once and not read back, so their
-    // stores are nontemporal
+    // lane (l16, g4) holds columns 4 g4 .. 4 g4 + 3 of block nb for token 16 rb + l16
     const unsigned ccol = (unsigned)h * a.Dv + (unsigned)(v0w + 4 * g4);
     if (a.out_all && n == kChunk) {  // every token of a full chunk is an output row, in stream order
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          __builtin_nontemporal_store(to_bf4(O[nb][rb]), reinterpret_cast<bf16x4*>(a.out + ((unsigned)t0 + 16 * rb + l16) * HDv + ccol + 16 * nb));
+          *reinterpret_cast<bf16x4*>(a.out + ((unsigned)t0 + 16 * rb + l16) * HDv + ccol + 16 * nb) = to_bf4(O[nb][rb]);
     } else {
       const int* sOR = reinterpret_cast<const int*>(tb + tOR);
 #pragma unroll
@@ -879,7 +877,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
         if (orow >= 0) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            __builtin_nontemporal_store(to_bf4(O[nb][rb]), reinterpret_cast<bf16x4*>(a.out + (unsigned)orow * HDv + ccol + 16 * nb));
+            *reinterpret_cast<bf16x4*>(a.out + (unsigned)orow * HDv + ccol + 16 * nb) = to_bf4(O[nb][rb]);
         }
       }
     }
