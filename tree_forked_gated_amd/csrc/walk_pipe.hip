@@ -50,6 +50,11 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+// Global-memory view of a state row. The entry-state pointer comes from a
+// descriptor in LDS, so the compiler cannot tell its address space; through a
+// generic pointer the loads would be flat loads, which also count against the
+// LDS wait counter and would hold up every later LDS wait.
+typedef __attribute__((address_space(1))) const f32x4 gf32x4;
 
 constexpr int DK = 128;
 constexpr int kXcd = kWalkQueues;  // workgroup b runs on XCD b % 8 of an MI355X
@@ -470,6 +475,7 @@ __device__ __forceinline__ void issue_kq(const Args& a, const Desc& d, unsigned 
 struct TokenRegs {
   unsigned short g, b;  // bf16 bits
   int par, om, sm, fs;
+  unsigned long long tm;  // ancestor-or-self mask of the token in a tree chunk
 };
 
 __device__ __forceinline__ TokenRegs load_tokens(const Args& a, const Desc& d, int lane) {
@@ -480,6 +486,10 @@ __device__ __forceinline__ TokenRegs load_tokens(const Args& a, const Desc& d, i
   r.om = kUnmapped;
   r.sm = kUnmapped;
   r.fs = -1;
+  r.tm = 0;
+  // the mask rows of a tree chunk are loaded here, with the other token values,
+  // so that their latency hides behind the chunk's products
+  if (d.valid && d.mode) r.tm = a.tree_mask[(size_t)d.sq * kChunk + lane];
   if (d.valid && lane < d.n) {
     const int t = d.t0 + lane;
     r.g = reinterpret_cast<const unsigned short*>(a.g)[(size_t)t * a.H + d.h];
@@ -532,7 +542,7 @@ __device__ __forceinline__ void store_tokens(const Args& a, Desc d, const TokenR
         pj = pp;
       }
     }
-    mask = a.tree_mask[(size_t)d.sq * kChunk + i];
+    mask = r.tm;
   } else {
     G = wave_prefix_sum(G);
     mask = (i == 63) ? ~0ull : ((2ull << i) - 1ull);
@@ -1008,7 +1018,7 @@ __device__ __forceinline__ void load_entry(const Desc* dp, int ws, int lane, f32
       const float* row = sin + (size_t)(16 * NB * ws + 16 * nb + l16) * DK + 8 * g4;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        T[nb][dt] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + 32 * (dt >> 1) + 4 * (dt & 1)));
+        T[nb][dt] = __builtin_nontemporal_load((const gf32x4*)(row + 32 * (dt >> 1) + 4 * (dt & 1)));
     }
   } else {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -1055,9 +1065,12 @@ __device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, i
   // wrote it one iteration earlier), so it is read before the barrier that
   // ends chunk it and the next chunk starts without an LDS round trip.
   SDesc cd = load_sdesc(smem + C::oTB + tD);
+  // An item's entry state is loaded before the barrier that precedes its first
+  // chunk (the previous item's state is dead by then), so that the load's
+  // latency passes while the wave waits at the barrier.
+  if (cd.valid && cd.first) load_entry<NB>(reinterpret_cast<const Desc*>(smem + C::oTB + tD), ws, lane, ST);
   for (int it = 0;; ++it) {
     const unsigned char* tb = smem + C::oTB + (it % 3) * kTB;
-    const Desc* dp = reinterpret_cast<const Desc*>(tb + tD);
     if (!cd.valid) break;
     const int t0 = cd.t0, n = cd.n, h = cd.h, v0 = cd.v0;
     const int mode = cd.mode;
@@ -1069,8 +1082,7 @@ __device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, i
     const unsigned char* pr = smem + C::oPR + (it & 1) * kPR;
     const int v0w = v0 + 16 * NB * ws;  // first column of the wave
 
-    if (first) {  // a new item: its entry state
-      load_entry<NB>(dp, ws, lane, ST);
+    if (first) {  // a new item: its entry state, loaded before the barrier
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -1080,7 +1092,9 @@ __device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, i
       state_chunk<BV, true>(a, smem, tb, kq, vt, pr, o, ST, Sb, it, t0, n, h, v0w, mode, need_exit, todo, lane);
     else
       state_chunk<BV, false>(a, smem, tb, kq, vt, pr, o, ST, Sb, it, t0, n, h, v0w, mode, need_exit, todo, lane);
-    cd = load_sdesc(smem + C::oTB + ((it + 1) % 3) * kTB + tD);
+    const Desc* dn = reinterpret_cast<const Desc*>(smem + C::oTB + ((it + 1) % 3) * kTB + tD);
+    cd = load_sdesc(reinterpret_cast<const unsigned char*>(dn));
+    if (cd.valid && cd.first) load_entry<NB>(dn, ws, lane, ST);
     lds_barrier();
   }
 }
