@@ -29,8 +29,8 @@
 //   the A tiles, the inverses of the diagonal blocks and the masked, decayed
 //   P = M . exp . Q K^T, and leave them in LDS as ready MFMA operands. They
 //   also copy q and k two chunks ahead and v one chunk ahead from HBM into LDS
-//   (direct-to-LDS loads), and the second helper walks the item list and
-//   prepares each chunk's token tables.
+//   (direct-to-LDS loads); the first helper also walks the item list and the
+//   second prepares each chunk's token tables.
 //
 // One barrier per chunk separates the stages. The state is kept transposed in
 // the MFMA accumulator layout, with its d_k index permuted so that the
@@ -716,6 +716,7 @@ __device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, 
     wait_vm();  // this wave's copies, token values and unit record have landed
     if (hid == 1) {
       store_tokens(a, nd, tr, smem + C::oTB + s2 * kTB, lane);
+    } else {
       Desc nn = {};
       if (nd.valid) nn = feed_next<BV>(ff, fr, a, xcd, count, base, lane);
       put_desc(reinterpret_cast<unsigned char*>(nds + ((it + 1) & 1)), nn, lane);
@@ -1127,7 +1128,7 @@ __global__ void __launch_bounds__(Cfg<BV>::NTHR, 1) k_walk_pipe(const Args a) {
   Feed ff;
   FeedRegs fr;
   feed_init(ff, fr, a);
-  if (hid == 1) {
+  if (hid == 0) {
 #pragma nounroll
     for (int i = 0; i < 2; ++i) {
       put_desc(reinterpret_cast<unsigned char*>(nds + i), feed_next<BV>(ff, fr, a, xcd, count, base, lane), lane);
