@@ -305,17 +305,32 @@ def main():
         parity["ok"] = all(v <= parity["tol"] for k, v in parity.items() if k not in ("tol",))
         log(f"parity vs oracle: {parity}")
 
+    copy_probe = None
     if args.copy_probe_mib > 0:
-        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
-        # under rocprofv3 --pmc calibrate the walk's counters
+        # plain copies of known size: their FETCH_SIZE / WRITE_SIZE per dispatch
+        # under rocprofv3 --pmc calibrate the walk's counters, and their time is
+        # the bandwidth a streaming kernel reaches on this part. Three buffer
+        # pairs rotate so that the last-level cache cannot serve a copy.
         nb = args.copy_probe_mib << 20
-        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
+        pairs = [(torch.ones(nb // 4, dtype=torch.float32, device=dev),
+                  torch.empty(nb // 4, dtype=torch.float32, device=dev)) for _ in range(3)]
+        for src, dst in pairs:
             dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"copy probe: 3 copies of {nb} bytes")
-        del src, dst
+        evc0, evc1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 12
+        evc0.record(stream)
+        for i in range(reps):
+            src, dst = pairs[i % 3]
+            dst.copy_(src)
+        evc1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * evc0.elapsed_time(evc1) / reps
+        copy_probe = {"bytes_per_copy": nb, "us_per_copy": round(us, 2),
+                      "read_plus_write_gbs": round(2 * nb / (us * 1e-6) / 1e9, 1)}
+        log(f"copy probe: 3 + {reps} copies of {nb} bytes; {us:.1f} us per copy, "
+            f"{copy_probe['read_plus_write_gbs']} GB/s read + write")
+        del pairs
 
     value = wl.T / (ms_step * 1e-3)
     line = {
@@ -333,6 +348,8 @@ def main():
         cc = commit_counts(wl)
         line["commit"] = {"ms": round(ms_commit, 5), "alg_bytes": cc["bytes"],
                           "hbm_frac": round(cc["bytes"] / (ms_commit * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    if copy_probe is not None:
+        line["copy_probe"] = copy_probe
     print(json.dumps(line), flush=True)
 
 
