@@ -9,7 +9,7 @@ cache cannot hold the next step's operands.
 
 Prints one JSON line (last line of stdout). Progress goes to stderr.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--graph]
 
 The default workload is 4 chains of 4096 tokens, 16 heads, d_k = d_v = 128;
 decision_round, draft_trees and mixed_forest are the other full-size streams.
@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--cpu-min-s", type=float, default=10.0,
                     help="repeat the CPU baseline over the whole workload for at least this long")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time whole steps replayed from captured graphs (one per input set)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (calibrates memory counters)")
     args = ap.parse_args()
@@ -248,6 +250,34 @@ def main():
     log(f"walk only: {ms_walk:.4f} ms/launch-set ({cap['max_levels']} level launches)"
         + (f"; commit {ms_commit:.4f} ms" if ms_commit is not None else ""))
 
+    graph = None
+    if args.graph:
+        # flat-graph replay: each input set's step captured once, then replayed
+        graphs = []
+        for x in sets:
+            fg = B.ForwardGraph(wl.T, wl.H, wl.Dk, wl.Dv, wl.n_seq, dt, max_forks=cap["max_forks"],
+                                max_levels=cap["max_levels"], n_out=None if out_rows is None else n_out,
+                                n_state=n_state, keep_pseudo=wl.keep_pseudo, n_path=wl.n_path if is_draft else 0,
+                                path_capacity=int(wl.path_ptr[-1]) if is_draft else 0, device=dev)
+            fg.load(x["q"], x["k"], x["v"], x["log_gate"], x["beta"], parent, seq_start, x["init_state"],
+                    out_rows=out_rows, state_rows=state_rows, path_ptr=pp if is_draft else None,
+                    path_nodes=pn if is_draft else None, path_seq=ps if is_draft else None)
+            graphs.append(fg.capture())
+        for i in range(len(graphs)):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+        ev6, ev7 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev6.record()
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        ev7.record()
+        torch.cuda.synchronize()
+        for fg in graphs:
+            fg.check()
+        graph = {"ms_per_step": round(ev6.elapsed_time(ev7) / args.steps, 5), "graphs": len(graphs)}
+        log(f"graph replay: {graph['ms_per_step']:.4f} ms/step")
+        del graphs
+
     cnt = algorithmic_counts(wl, n_out, n_state, wl.keep_pseudo)
     walk_gbs = cnt["bytes"] / (ms_walk * 1e-3) / 1e9
     walk_tflops = cnt["flops"] / (ms_walk * 1e-3) / 1e12
@@ -350,6 +380,8 @@ def main():
                           "hbm_frac": round(cc["bytes"] / (ms_commit * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if copy_probe is not None:
         line["copy_probe"] = copy_probe
+    if graph is not None:
+        line["graph_replay"] = graph
     print(json.dumps(line), flush=True)
 
 

@@ -346,3 +346,119 @@ def commit(k, log_gate, parent_idx, seq_start, init_state, pseudo_v, path_ptr, p
     if check:
         raise_device_error(workspace, stream)
     return out_state
+
+
+# -------------------------------------------------------------- graph replay
+
+class ForwardGraph:
+    """One captured forward (and optionally one commit) per size bucket,
+    replayed for any tree that fits the bucket.
+
+    Flide ("Accelerating Decision Inference with Exact State Forking", §3.3)
+    captures a flat graph per stream-capacity bucket and replays it for every
+    decision round. That works here because the tree is device data: the
+    metadata kernels rebuild segments, fork slots, levels and masks from
+    ``parent_idx`` inside the graph, and every launch shape depends only on
+    the bucket (T, H, d_k, d_v, n_seq, the fork and level capacities, the
+    numbers of output and state rows, and the number of commit paths), never
+    on the tree. Levels beyond the tree's own are launched and exit at once.
+
+    The buffers are static: ``load`` copies a round's tensors into them (with
+    torch copies on the current stream, outside the graph), ``replay`` runs
+    the captured kernels, and the results are read from ``out``, ``state_out``,
+    ``pseudo_v`` and ``committed``. A tree that needs more fork slots or
+    levels than the bucket holds is reported through the device error word
+    (``check``), as in an eager call. The graph holds only kernel launches of
+    this library (no memset nodes)."""
+
+    def __init__(self, T, H, Dk, Dv, n_seq, dtype, *, max_forks, max_levels, n_out=None, n_state=0,
+                 keep_pseudo=False, n_path=0, path_capacity=0, device="cuda"):
+        dev = torch.device(device)
+        self.device = dev
+        self.dtype = dtype
+        self.max_forks, self.max_levels = int(max_forks), max(1, int(max_levels))
+        self.keep_pseudo = bool(keep_pseudo) or n_path > 0
+        e = lambda *shape, dt=dtype: torch.zeros(shape, dtype=dt, device=dev)
+        self.q, self.k = e(T, H, Dk), e(T, H, Dk)
+        self.v = e(T, H, Dv)
+        self.log_gate, self.beta = e(T, H), e(T, H)
+        self.parent_idx = torch.full((T,), -1, dtype=torch.int32, device=dev)
+        self.seq_start = torch.zeros(n_seq + 1, dtype=torch.int32, device=dev)
+        self.init_state = e(n_seq, H, Dv, Dk, dt=torch.float32)
+        self.out_rows = None if n_out is None else torch.zeros(n_out, dtype=torch.int32, device=dev)
+        self.state_rows = torch.zeros(n_state, dtype=torch.int32, device=dev)
+        self.out = e(T if n_out is None else n_out, H, Dv)
+        self.state_out = e(n_state, H, Dv, Dk, dt=torch.float32)
+        self.pseudo_v = e(T, H, Dv, dt=torch.float32) if self.keep_pseudo else None
+        dims = make_dims(T, H, Dk, Dv, n_seq, _dtype_code(dtype), self.max_forks, self.max_levels)
+        self.workspace = alloc_workspace(dims, dev)
+        self.n_path = int(n_path)
+        if self.n_path:
+            self.path_ptr = torch.zeros(n_path + 1, dtype=torch.int32, device=dev)
+            self.path_nodes = torch.zeros(max(1, int(path_capacity)), dtype=torch.int32, device=dev)
+            self.path_seq = torch.zeros(n_path, dtype=torch.int32, device=dev)
+            self.committed = e(n_path, H, Dv, Dk, dt=torch.float32)
+            self.commit_workspace = torch.empty(int(lib.gdn_tree_commit_workspace_size()), dtype=torch.uint8,
+                                                device=dev)
+        self.graph = None
+
+    def load(self, q, k, v, log_gate, beta, parent_idx, seq_start, init_state=None, *, out_rows=None,
+             state_rows=None, path_ptr=None, path_nodes=None, path_seq=None):
+        """Copy one round into the static buffers (shapes must match the bucket;
+        path_nodes may be shorter than the path capacity)."""
+        for dst, src in ((self.q, q), (self.k, k), (self.v, v), (self.log_gate, log_gate), (self.beta, beta)):
+            dst.copy_(src)
+        self.parent_idx.copy_(_i32(parent_idx, self.device))
+        self.seq_start.copy_(_i32(seq_start, self.device))
+        if init_state is None:
+            self.init_state.zero_()
+        else:
+            self.init_state.copy_(init_state)
+        if self.out_rows is not None:
+            self.out_rows.copy_(_i32(out_rows, self.device))
+        if self.state_rows.numel():
+            self.state_rows.copy_(_i32(state_rows, self.device))
+        if self.n_path:
+            nodes = _i32(path_nodes, self.device)
+            if nodes.numel() > self.path_nodes.numel():
+                raise GdnError(f"{nodes.numel()} path nodes exceed the bucket's capacity {self.path_nodes.numel()}")
+            self.path_ptr.copy_(_i32(path_ptr, self.device))
+            self.path_nodes[:nodes.numel()].copy_(nodes)
+            self.path_seq.copy_(_i32(path_seq, self.device))
+
+    def _launch(self):
+        forward(self.q, self.k, self.v, self.log_gate, self.beta, self.parent_idx, self.seq_start, self.init_state,
+                out_rows=self.out_rows, state_rows=self.state_rows, keep_pseudo=self.keep_pseudo,
+                max_forks=self.max_forks, max_levels=self.max_levels, workspace=self.workspace, out=self.out,
+                state_out=self.state_out, pseudo_v=self.pseudo_v)
+        if self.n_path:
+            commit(self.k, self.log_gate, self.parent_idx, self.seq_start, self.init_state, self.pseudo_v,
+                   self.path_ptr, self.path_nodes, self.path_seq, workspace=self.commit_workspace,
+                   out_state=self.committed)
+
+    def capture(self):
+        """Capture the forward (and commit) on the loaded buffers. One eager run
+        on a side stream comes first, so that nothing is initialised during
+        capture."""
+        s = torch.cuda.Stream(device=self.device)
+        s.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(s):
+            self._launch()
+        torch.cuda.current_stream(self.device).wait_stream(s)
+        torch.cuda.synchronize(self.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self._launch()
+        self.graph = g
+        return self
+
+    def replay(self):
+        if self.graph is None:
+            raise GdnError("ForwardGraph.replay before capture")
+        self.graph.replay()
+
+    def check(self, stream=None):
+        """Raise the device error of the last replay, if any (synchronises)."""
+        raise_device_error(self.workspace, stream)
+        if self.n_path:
+            raise_device_error(self.commit_workspace, stream)
