@@ -102,8 +102,7 @@ struct Cfg {
   static constexpr int oPP = oPR + 2 * kPR;      // [3] P
   static constexpr int oLT = oPP + 3 * kPP;      // diagonal-block staging
   static constexpr int oND = oLT + 4 * kLTS * 4; // [2] descriptors of chunks to copy, by parity
-  static constexpr int oTR = oND + 128;          // 1 KB that L2 prefetches land in (never read)
-  static constexpr int bytes = oTR + 1024;
+  static constexpr int bytes = oND + 128;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(oTB % 16 == 0 && oV % 16 == 0 && oPR % 16 == 0 && oPP % 16 == 0 && oLT % 16 == 0 && oND % 16 == 0,
                 "alignment");
@@ -444,19 +443,25 @@ __device__ __forceinline__ void issue_v(const Args& a, const Desc& d, unsigned c
 }
 
 // The entry state rows of the next chunk's d_v tile (BV rows of d_k fp32,
-// contiguous) are pulled into L2 while the current chunk runs: the copies land
-// in a scratch kilobyte of LDS that nobody reads, so that the state waves'
-// own loads of those rows hit L2. The two helpers take alternate kilobytes.
+// contiguous, BV * 512 bytes) are pulled into L2 while the current chunk runs,
+// so that the state waves' own loads of those rows hit L2: each lane loads one
+// word of a different 128-byte line, the two helpers taking alternate halves
+// (one or two loads per helper instead of BV / 4 direct-to-LDS copies). The
+// words are consumed only after the helper's own wait for its copies, so the
+// loads never hold the wave up.
+struct Touch {
+  unsigned w0, w1;
+};
+typedef __attribute__((address_space(1))) const unsigned gu32;
 template <int BV>
-__device__ __forceinline__ void prefetch_entry(const float* sin, unsigned char* trash, int hid, int lane) {
-  const uint32_t l = lds_addr_of(trash);
-  unsigned vo = (unsigned)lane * 16u + (unsigned)hid * 1024u;
-#pragma unroll
-  for (int k = 0; k < BV / 4; ++k) {  // BV * 512 bytes = BV / 2 kilobytes, half per helper
-    dma16(sin, vo, l);
-    vo += 2048u;
-  }
+__device__ __forceinline__ Touch prefetch_entry(const float* sin, int hid, int lane) {
+  constexpr int kPer = BV * 2;  // lines per helper: BV rows x 4 lines / 2
+  Touch t = {0u, 0u};
+  if (lane < kPer) t.w0 = *(gu32*)(sin + (size_t)(hid * kPer + lane) * 32);
+  if (kPer > 64 && lane + 64 < kPer) t.w1 = *(gu32*)(sin + (size_t)(hid * kPer + 64 + lane) * 32);
+  return t;
 }
+__device__ __forceinline__ void consume(const Touch& t) { asm volatile("" ::"v"(t.w0), "v"(t.w1)); }
 
 // Helper 0 copies K and the first kQSplit blocks of 4 rows of Q, helper 1 the
 // rest of Q (helper 0 also inverts the diagonal blocks, so it takes fewer copies).
@@ -709,11 +714,13 @@ __device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, 
     if (hid == 1) tr = load_tokens(a, nd, lane);
     if (nd.valid) issue_kq(a, nd, smem + C::oKQ + s2 * 32768, hid, lane);
     if (hid == 1 && nx.valid) issue_v<BV>(a, nx, smem + C::oV + ((it + 1) & 1) * C::VT, lane);
-    if (nx.valid && nx.first && nx.sin) prefetch_entry<BV>(nx.sin, smem + C::oTR, hid, lane);
+    Touch touch = {0u, 0u};
+    if (nx.valid && nx.first && nx.sin) touch = prefetch_entry<BV>(nx.sin, hid, lane);
     if (nx.valid)
       chunk_products(hid, nx, smem + C::oKQ + s1 * 32768, tb1, smem + C::oPR + ((it + 1) & 1) * kPR,
                      smem + C::oPP + s1 * kPP, lt, lane);
     wait_vm();  // this wave's copies, token values and unit record have landed
+    consume(touch);
     if (hid == 1) {
       store_tokens(a, nd, tr, smem + C::oTB + s2 * kTB, lane);
     } else {
