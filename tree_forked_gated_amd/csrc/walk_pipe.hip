@@ -745,7 +745,7 @@ struct SOff {
 // dst = cS src + (K^T rows of the state block) x (decayed pseudo-values w) for
 // every 16-column block and d_k tile; dst may be src (each tile depends only on
 // its own tile of src).
-template <int NB>
+template <int NB, bool SCALE = true>
 __device__ __forceinline__ void state_at(f32x4 (&dst)[NB][8], const f32x4 (&src)[NB][8], float cS, const unsigned char* kq,
                                          const SOff<NB>& o, const bf16x8 (&w01)[NB], const bf16x8 (&w23)[NB]) {
 #pragma unroll
@@ -758,7 +758,7 @@ __device__ __forceinline__ void state_at(f32x4 (&dst)[NB][8], const f32x4 (&src)
     for (int nb = 0; nb < NB; ++nb) {
       f32x4 t;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) t[r] = cS * src[nb][dt][r];
+      for (int r = 0; r < 4; ++r) t[r] = SCALE ? cS * src[nb][dt][r] : src[nb][dt][r];
       t = mma32(k01, w01[nb], t);
       dst[nb][dt] = mma32(k23, w23[nb], t);
     }
@@ -822,6 +822,23 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
 #pragma unroll
       for (int m = 0; m < 4; ++m) X[nb][rb] = mma32(KF[m], Sb[nb][m], X[nb][rb]);
     }
+  }
+  // When the chunk exit is the only state asked for, S is scaled by the exit's
+  // decay e^{G_{n-1}} here, next to the matrix products, instead of inside the
+  // exit update at the end of the chunk's dependency chain (S itself is not
+  // read again before the exit: K S^T and S Q^T use its bf16 copy). Only for
+  // waves of one 16-column block: with two, the extra path cost scalar-register
+  // spills and made the 64-column walk slower.
+  bool prescale = false;
+  if constexpr (NB == 1) prescale = need_exit && todo == (1ull << (n - 1));
+  if (prescale) {
+    const float cs = sEG[n - 1];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ST[nb][dt][r] *= cs;
   }
   // Scheduling barriers between the stages keep the compiler from hoisting every
   // stage's LDS reads to the top of the chunk, which pushed values out to AGPRs
@@ -1000,7 +1017,12 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
     const int sr = reinterpret_cast<const int*>(tb + tSR)[p];
     if (need_exit && p == n - 1) {
       // the chunk exit (always the last requested token): S is updated in place
-      state_at<NB>(ST, ST, cS, kq, o, w01, w23);
+      if constexpr (NB == 1) {
+        if (prescale) state_at<NB, false>(ST, ST, cS, kq, o, w01, w23);
+        else state_at<NB>(ST, ST, cS, kq, o, w01, w23);
+      } else {
+        state_at<NB>(ST, ST, cS, kq, o, w01, w23);
+      }
       store_state<NB>(a, ST, fs, sr, h, v0w, lane);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
