@@ -127,3 +127,36 @@ def test_graph_replay_draft_trees_with_commit():
         assert _same(fg.out, ref.out), f"replay {step} (round {i}): outputs differ"
         assert _same(fg.pseudo_v, ref.pseudo_v), f"replay {step} (round {i}): pseudo-values differ"
         assert _same(fg.committed, st), f"replay {step} (round {i}): committed states differ"
+
+
+def test_graph_replay_reports_a_tree_beyond_its_bucket():
+    """A round that needs more levels than the bucket holds is reported through
+    the device error word (the walk then computes nothing); the next round that
+    fits replays correctly from the same graph."""
+    from tree_forked_gated_amd import binding as B
+    lens, H, D = [300, 64, 150], 4, 128
+    rounds = {s: _round(s, lens, H, D, "bf16", 48, 12) for s in (11, 12)}
+    caps = {s: B.capacities(r["parent"], r["seq_start"]) for s, r in rounds.items()}
+    mf = max(c["max_forks"] for c in caps.values())
+    ml = caps[11]["max_levels"]
+    assert caps[12]["max_levels"] > ml, caps
+    say(f"bucket: forks {mf}, levels {ml}; round 12 needs {caps[12]['max_levels']} levels")
+    fg = B.ForwardGraph(sum(lens), H, D, D, len(lens), torch.bfloat16, max_forks=mf, max_levels=ml, n_out=48,
+                        n_state=12, keep_pseudo=True)
+    fg.load(**_dev(rounds[11], torch.bfloat16))
+    fg.capture()
+    fg.load(**_dev(rounds[12], torch.bfloat16))
+    fg.replay()
+    torch.cuda.synchronize()
+    with pytest.raises(B.GdnDeviceError) as ei:
+        fg.check()
+    assert ei.value.code == 5, ei.value  # level capacity
+    d = _dev(rounds[11], torch.bfloat16)
+    fg.load(**d)
+    fg.replay()
+    ref = B.forward(d["q"], d["k"], d["v"], d["log_gate"], d["beta"], d["parent_idx"], d["seq_start"],
+                    d["init_state"], out_rows=d["out_rows"], state_rows=d["state_rows"], keep_pseudo=True,
+                    max_forks=mf, max_levels=ml)
+    torch.cuda.synchronize()
+    fg.check()
+    assert _same(fg.out, ref.out) and _same(fg.state_out, ref.state) and _same(fg.pseudo_v, ref.pseudo_v)
