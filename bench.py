@@ -83,12 +83,13 @@ def commit_counts(wl):
 # -------------------------------------------------------------------- traffic
 
 def source_digest():
-    """Digest of the sources that define the walk kernel (its traffic does not
-    depend on the metadata or commit kernels)."""
+    """Digest of the sources that define the walk kernel and of the build script
+    that sets its compiler flags (its traffic does not depend on the metadata
+    or commit kernels)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "tree_forked_gated_amd", "csrc")
-    for name in ("gdn_internal.h", "walk_pipe.hip"):
-        h.update(open(os.path.join(csrc, name), "rb").read())
+    pkg = os.path.join(ROOT, "tree_forked_gated_amd")
+    for name in ("csrc/gdn_internal.h", "csrc/walk_pipe.hip", "build.py"):
+        h.update(open(os.path.join(pkg, name), "rb").read())
     return h.hexdigest()[:16]
 
 
