@@ -792,6 +792,16 @@ __device__ __forceinline__ void store_state(const Args& a, const f32x4 (&S)[NB][
   }
 }
 
+// Boundary between two stages of a state wave's chunk. For waves of one
+// 16-column block a scheduling barrier keeps the compiler from hoisting every
+// stage's LDS reads to the top of the chunk (values then went out to AGPRs and
+// back; 1-3% slower without it); waves of two blocks schedule better without
+// it under the ILP schedule (mixed forest 2.3% faster).
+template <int NB>
+__device__ __forceinline__ void stage_fence() {
+  if constexpr (NB == 1) __builtin_amdgcn_sched_barrier(0);
+}
+
 // One chunk on a state wave: K S_e^T, R, the block substitution, the outputs
 // and pseudo-values, then the states after requested tokens and at the exit.
 // The wave owns NB blocks of 16 columns. ST[nb][dt] (dt = 2 m + bb) holds S^T
@@ -842,10 +852,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
 #pragma unroll
         for (int r = 0; r < 4; ++r) ST[nb][dt][r] *= cs;
   }
-  // Scheduling barriers between the stages keep the compiler from hoisting every
-  // stage's LDS reads to the top of the chunk, which pushed values out to AGPRs
-  // and back (measured 1-3% faster with them).
-  __builtin_amdgcn_sched_barrier(0);
+  stage_fence<NB>();
   // e^G S_e Q^T (the output, transposed): lane holds four columns of one token
   f32x4 O[NB][4];
   if (HAS_OUT) {
@@ -865,7 +872,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
       }
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
+  stage_fence<NB>();
   // R = beta (V - e^G K S^T) in place of X
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
@@ -880,7 +887,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
       X[nb][rb][3] = bi.w * ((float)vb[3] - eg.w * X[nb][rb][3]);
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
+  stage_fence<NB>();
   // block substitution with the helpers' -A_bm and (I + A_bb)^{-1}
   bf16x4 nA[6], DI[4];
 #pragma unroll
@@ -906,7 +913,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
     Vt[nb][3] = mma16(DI[3], to_bf4(y), zero);
     Vb[nb][3] = to_bf4(Vt[nb][3]);
   }
-  __builtin_amdgcn_sched_barrier(0);
+  stage_fence<NB>();
   if (HAS_OUT) {
     // O^T += Vt^T P^T over pairs of 16-token blocks (blocks of P above the
     // diagonal are zero; the helpers' P fragments are the B operands)
@@ -943,7 +950,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
       }
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
+  stage_fence<NB>();
   if (a.pv) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -962,7 +969,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
       }
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
+  stage_fence<NB>();
   // states after requested tokens (fork slots, state rows) and at the chunk exit
   if (!todo) return;
   const float* sG2 = reinterpret_cast<const float*>(tb + tG2);
