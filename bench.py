@@ -117,7 +117,7 @@ def measured_traffic(workload_name):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chains", choices=["chains", "decision_round", "draft_trees", "mixed_forest"])
     ap.add_argument("--rotate", type=int, default=3, help="independent input sets cycled between steps")
@@ -215,14 +215,23 @@ def main():
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    # an event between consecutive steps gives each step's time as well (the
+    # events are recorded between launches on the same stream: no host sync)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     ev0.record(stream)
+    evs[0].record(stream)
     for i in range(args.steps):
         step(i)
+        evs[i + 1].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step (events), wall {1e3 * wall / args.steps:.4f} ms/step")
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    step_pct = {"p10": round(float(np.percentile(per_step, 10)), 5), "p50": round(float(np.median(per_step)), 5),
+                "p90": round(float(np.percentile(per_step, 90)), 5)}
+    log(f"timed {args.steps} steps: {ms_step:.4f} ms/step (events), wall {1e3 * wall / args.steps:.4f} ms/step; "
+        f"per step p10/p50/p90 {step_pct['p10']:.4f}/{step_pct['p50']:.4f}/{step_pct['p90']:.4f} ms")
     for x in sets:
         B.raise_device_error(x["ws"], stream)
 
@@ -374,6 +383,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
+        "step_ms_percentiles": step_pct,
     }
     if ms_commit is not None:
         cc = commit_counts(wl)
