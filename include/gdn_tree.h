@@ -30,6 +30,13 @@
  *  - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
  *    work; they return before it runs and never synchronise, except
  *    gdn_tree_check_error.
+ *  - gdn_tree_forward, gdn_tree_plan and gdn_tree_commit enqueue kernel
+ *    launches only (no memset, copy or allocation), and their launch shapes
+ *    depend on the sizes and capacities in the arguments, never on the tree.
+ *    They can therefore be captured once in a HIP graph and replayed for any
+ *    tree that fits the same sizes and capacities (Flide section 3.3 replays
+ *    one flat graph per capacity bucket this way): the metadata is rebuilt
+ *    from parent_idx on every replay.
  *  - The caller owns every buffer, the workspace included, and keeps them
  *    alive until the stream has passed the call. The library allocates no
  *    device memory and keeps no mutable global state besides a thread-local
