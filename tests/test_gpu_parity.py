@@ -116,3 +116,15 @@ def test_planned_walk_is_bitwise_the_full_forward():
     code, _ = B.check_error(ws)
     assert code == 8
     assert bool((st3 == 7.0).all())
+
+
+@pytest.mark.parametrize("seed", [100, 107, 113, 121, 128, 136])
+def test_random_forests_dk128_every_tile(seed):
+    """Random chains, draft trees and nested forests at d_k = 128 in bf16 (the
+    pipelined walk), every d_v tile width that divides d_v, all leaf states."""
+    rng = np.random.default_rng(seed)
+    Dv = int(rng.choice([16, 32, 64, 128]))
+    H = int(rng.integers(1, 4))
+    wl = W.random_small(seed, n_seq=int(rng.integers(1, 6)), H=H, Dk=128, Dv=Dv, dtype="bf16", max_len=400)
+    for dv_tile in [0] + [t for t in (16, 32, 64) if Dv % t == 0]:
+        _check(wl, f"random_dk128[{seed}] tile {dv_tile}", dv_tile=dv_tile)
