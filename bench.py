@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=0)
     ap.add_argument("--cpu-min-s", type=float, default=10.0,
                     help="repeat the CPU baseline over the whole workload for at least this long")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="also measure the achievable bf16 MFMA rate with an independent-MFMA loop")
     ap.add_argument("--graph", action="store_true",
                     help="also time whole steps replayed from captured graphs (one per input set)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -320,10 +322,18 @@ def main():
             refc = oracle.commit(wl, "f32", n_threads=threads) if is_draft else None
             passes += 1
             cpu_s = time.perf_counter() - t0
+        model = "unknown CPU"
+        try:
+            for ln in open("/proc/cpuinfo"):
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         cpu = {"value": round(passes * wl.T / cpu_s, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"{passes} whole passes over the {wl.name} workload ({wl.T} tokens x {wl.H} heads), "
                          f"fp32 per-token parent walk" + (" + replay commit" if is_draft else "")
-                         + f", {cpu_s:.2f} s wall"}
+                         + f", {cpu_s:.2f} s wall on {threads} threads of {model}"}
         log(f"cpu baseline: {passes} passes in {cpu_s:.2f} s on {threads} threads")
         x = sets[0]
         step(0)
@@ -372,6 +382,32 @@ def main():
             f"{copy_probe['read_plus_write_gbs']} GB/s read + write")
         del pairs
 
+    mfma_probe = None
+    if args.mfma_probe:
+        # achievable matrix-core rate: eight independent MFMA chains per wave,
+        # four waves per SIMD on every CU (a library of its own, not the ABI)
+        import ctypes
+        plib = ctypes.CDLL(os.path.join(ROOT, "tree_forked_gated_amd", "probe", "libgdn_probe.so"))
+        plib.gdn_probe_mfma_flops.restype = ctypes.c_double
+        blocks, iters = 4 * torch.cuda.get_device_properties(dev).multi_processor_count, 2000
+        pout = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        run = lambda: plib.gdn_probe_mfma(ctypes.c_void_p(pout.data_ptr()), blocks, iters, sp)
+        if run() != 0:
+            raise RuntimeError("MFMA probe launch failed")
+        torch.cuda.synchronize()
+        evp0, evp1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        evp0.record(stream)
+        for _ in range(5):
+            run()
+        evp1.record(stream)
+        torch.cuda.synchronize()
+        ms_p = evp0.elapsed_time(evp1) / 5
+        tf = plib.gdn_probe_mfma_flops(blocks, iters) / (ms_p * 1e-3) / 1e12
+        mfma_probe = {"tflops": round(tf, 1), "frac_of_nominal": round(tf / BF16_PEAK_TFLOPS, 4),
+                      "ms": round(ms_p, 4), "blocks": blocks, "iters": iters}
+        log(f"MFMA probe: {tf:.1f} TFLOP/s bf16 ({100 * tf / BF16_PEAK_TFLOPS:.1f}% of {BF16_PEAK_TFLOPS:.0f})")
+
     value = wl.T / (ms_step * 1e-3)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -393,6 +429,8 @@ def main():
         line["copy_probe"] = copy_probe
     if graph is not None:
         line["graph_replay"] = graph
+    if mfma_probe is not None:
+        line["mfma_probe"] = mfma_probe
     print(json.dumps(line), flush=True)
 
 
