@@ -83,13 +83,16 @@ def commit_counts(wl):
 # -------------------------------------------------------------------- traffic
 
 def source_digest():
-    """Digest of the sources that define the walk kernel and of the build script
-    that sets its compiler flags (its traffic does not depend on the metadata
-    or commit kernels)."""
+    """Digest of what defines the walk kernel's code: its sources and the
+    compiler flags it is built with (its traffic does not depend on the
+    metadata or commit kernels)."""
+    from tree_forked_gated_amd import build as hipbuild
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "tree_forked_gated_amd")
-    for name in ("csrc/gdn_internal.h", "csrc/walk_pipe.hip", "build.py"):
+    for name in ("csrc/gdn_internal.h", "csrc/walk_pipe.hip"):
         h.update(open(os.path.join(pkg, name), "rb").read())
+    flags = [f for f in hipbuild.FLAGS if not f.startswith(ROOT)] + hipbuild.FILE_FLAGS.get("walk_pipe.hip", [])
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
