@@ -140,7 +140,7 @@ def test_graph_replay_reports_a_tree_beyond_its_bucket():
     mf = max(c["max_forks"] for c in caps.values())
     ml = caps[11]["max_levels"]
     assert caps[12]["max_levels"] > ml, caps
-    say(f"bucket: forks {mf}, levels {ml}; round 12 needs {caps[12]['max_levels']} levels")
+    say(f"bucket: forks {mf}, levels {ml}; the round of seed 12 needs {caps[12]['max_levels']} levels")
     fg = B.ForwardGraph(sum(lens), H, D, D, len(lens), torch.bfloat16, max_forks=mf, max_levels=ml, n_out=48,
                         n_state=12, keep_pseudo=True)
     fg.load(**_dev(rounds[11], torch.bfloat16))
