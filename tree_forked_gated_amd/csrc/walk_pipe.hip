@@ -723,9 +723,8 @@ __device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, 
                      smem + C::oPP + s1 * kPP, lt, lane);
     wait_vm();  // this wave's copies, token values and unit record have landed
     consume(touch);
-    if (hid == 1) {
-      store_tokens(a, nd, tr, smem + C::oTB + s2 * kTB, lane);
-    } else {
+    if (hid == 1) store_tokens(a, nd, tr, smem + C::oTB + s2 * kTB, lane);
+    if (hid == 0) {
       Desc nn = {};
       if (nd.valid) nn = feed_next<BV>(ff, fr, a, xcd, count, base, lane);
       put_desc(reinterpret_cast<unsigned char*>(nds + ((it + 1) & 1)), nn, lane);
