@@ -11,8 +11,17 @@ Prints one JSON line (last line of stdout). Progress goes to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--graph]
 
-The default workload is 4 chains of 4096 tokens, 16 heads, d_k = d_v = 128;
-decision_round, draft_trees and mixed_forest are the other full-size streams.
+The default (headline) workload is the largest single-GPU stream: 65,536 tokens
+of seeded nested forests in one flat stream, 32 heads, d_k = d_v = 128, bf16
+inputs with fp32 state. chains (4 x 4096 tokens, 16 heads), decision_round
+(8 x (8192 + 16 x 32) tokens, 16 heads) and draft_trees (64 trees x 64 nodes,
+32 heads, with commit) are the other full-size streams, selected with
+--workload.
+
+The roofline's dominant kernel is the walk (k_walk_pipe). A forward launches it
+once per fork level of the tree (four on the forest), so its unit is one
+forward's walk: every level launch of one step. `achieved` divides the step's
+algorithmic bytes (or flops) by the HIP-event time of those launches.
 """
 from __future__ import annotations
 
@@ -97,8 +106,9 @@ def source_digest():
 
 
 def measured_traffic(workload_name):
-    """HBM bytes per walk launch from the committed rocprofv3 counter summary,
-    or None when there is none or the kernels changed since it was taken."""
+    """HBM bytes of one forward's walk (all its level launches) from the
+    committed rocprofv3 counter summary, or None when there is none or the
+    kernels changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"walk_traffic_{workload_name}.md")
     if not os.path.exists(path):
         return None
@@ -122,7 +132,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="chains", choices=["chains", "decision_round", "draft_trees", "mixed_forest"])
+    ap.add_argument("--workload", default="mixed_forest",
+                    choices=["mixed_forest", "chains", "decision_round", "draft_trees"])
     ap.add_argument("--rotate", type=int, default=3, help="independent input sets cycled between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
@@ -305,7 +316,9 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(walk_tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(walk_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
-    roof.update({"kernel": "k_walk_pipe" if wl.dtype == "bf16" and wl.Dk == 128 else "k_walk", "launches_per_step": cap["max_levels"], "ms_per_step": round(ms_walk, 5),
+    roof.update({"kernel": "k_walk_pipe" if wl.dtype == "bf16" and wl.Dk == 128 else "k_walk",
+                 "unit": "one forward's walk: every level launch of a step",
+                 "launches_per_step": cap["max_levels"], "ms_per_step": round(ms_walk, 5),
                  "alg_bytes": cnt["bytes"], "alg_flops": cnt["flops"],
                  "mfma_frac": round(walk_tflops / BF16_PEAK_TFLOPS, 4),
                  "hbm_frac": round(walk_gbs / HBM_PEAK_GBS, 4)})

@@ -107,7 +107,8 @@ typedef enum gdn_dev_error {
 /*
  * Sizes of one forward call.
  *  T          tokens in the flat stream (<= 2^31 - 1)
- *  H          heads (>= 1); every head has its own q, k, v, gate, beta and state
+ *  H          heads (>= 1); every head has its own q, k, v, gate, beta and state;
+ *             H * max(Dk, Dv) must stay below 2^24 (GDN_ERR_DIMS otherwise)
  *  Dk, Dv     key and value widths. bf16: Dk in {32, 64, 128}; fp32: Dk in
  *             {16, 32, 64}. Dv: a multiple of 16, at most 128.
  *  n_seq      sequences; seq_start has n_seq + 1 entries
@@ -182,7 +183,11 @@ typedef struct gdn_tree_fwd_args {
  *  pseudo_v             [T, H, Dv] fp32 written by that forward
  *  n_path, path_ptr [n_path+1], path_nodes   CSR of accepted paths; each lists global token
  *                       indices from a root (parent -1) down to the accepted node, each node
- *                       the parent of the next; an empty path commits the initial state
+ *                       the parent of the next; an empty path commits the initial state.
+ *                       path_nodes is required whenever n_path > 0 (any valid address when
+ *                       every path is empty). Every node is checked against its sequence's
+ *                       range inside [0, T) before anything indexed by it is read; a bad path
+ *                       raises GDN_DEV_PATH (the smallest such path) and its state is not written.
  *  path_seq [n_path]    sequence of each path
  *  out_state            [n_path, H, Dv, Dk] fp32
  *  workspace            device buffer of at least gdn_tree_commit_workspace_size() bytes

@@ -19,7 +19,7 @@ import torch
 
 from tree_forked_gated_amd import workloads as W
 
-from gpu_helpers import f64, oracle_ref, rel_l2, run_forward, say, tol
+from gpu_helpers import f64, oracle_ref, record_margin, rel_l2, run_forward, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,7 @@ def _rows_ok(gpu, ref, what):
     worst = float(err.max() / max(scale, 1e-30))
     say(f"  {what}: worst row error {worst:.3e} of the typical row norm")
     assert worst <= ROW_TOL, (what, worst)
+    return worst
 
 
 @pytest.mark.parametrize("name", ["chains", "decision_round", "draft_trees", "mixed_forest"])
@@ -53,10 +54,10 @@ def test_full_size_against_oracle(name):
     if wl.keep_pseudo:
         errs["pseudo_v"] = rel_l2(f64(res.pseudo_v), ref["pseudo_v"])
     say(f"  rel-L2 {errs}")
+    worst = {"out_worst_row": _rows_ok(out, ref_out, "out"), "state_worst_row": _rows_ok(st, ref["state"], "state")}
+    record_margin(f"full_size/{wl.name}", tol=tol(wl), row_tol=ROW_TOL, **errs, **worst)
     for k, e in errs.items():
         assert e <= tol(wl), (name, k, e)
-    _rows_ok(out, ref_out, "out")
-    _rows_ok(st, ref["state"], "state")
     if wl.path_ptr is not None:  # draft trees: commit the accepted paths
         import oracle
         from tree_forked_gated_amd import binding as B
@@ -66,8 +67,9 @@ def test_full_size_against_oracle(name):
         refc = oracle.commit(wl, "f64")
         e = rel_l2(f64(got), refc)
         say(f"  commit rel-L2 {e:.3e}")
+        wc = _rows_ok(f64(got), refc, "commit")
+        record_margin(f"full_size/{wl.name}/commit", tol=tol(wl), commit=e, commit_worst_row=wc)
         assert e <= tol(wl)
-        _rows_ok(f64(got), refc, "commit")
 
 
 def _stream(lens, forks=(), H=3, D=128, seed=77):
@@ -117,6 +119,7 @@ def test_empty_stream():
     e = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)
     res = B.forward(e(0, 2, 128), e(0, 2, 128), e(0, 2, 128), e(0, 2), e(0, 2),
                     torch.zeros(0, dtype=torch.int32, device=dev), torch.zeros(2, dtype=torch.int32, device=dev),
-                    torch.zeros((1, 2, 128, 128), dtype=torch.float32, device=dev), check=True)
+                    torch.zeros((1, 2, 128, 128), dtype=torch.float32, device=dev), max_forks=0, max_levels=1,
+                    check=True)
     torch.cuda.synchronize()
     assert res.out.shape[0] == 0

@@ -10,7 +10,7 @@ import pytest
 
 from tree_forked_gated_amd import workloads as W
 
-from gpu_helpers import f64, oracle_ref, rel_l2, run_forward, say, tol
+from gpu_helpers import f64, oracle_ref, record_margin, rel_l2, run_forward, say, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -26,6 +26,7 @@ def _check(wl, name, dv_tile=0, pseudo=True):
     if pseudo:
         errs["pseudo_v"] = rel_l2(f64(res.pseudo_v), ref["pseudo_v"])
     say(f"  rel-L2 {errs}")
+    record_margin(f"parity/{name}", tol=tol(wl), **errs)
     for k, e in errs.items():
         assert e <= tol(wl), (name, k, e)
     return res, ref

@@ -66,8 +66,8 @@ def test_plan_full_size_structures():
         _compare(wl.parent, wl.seq_start)
 
 
-@pytest.mark.parametrize("case", ["order", "self", "below", "crossseq", "seqstart", "seqlast", "forkcap", "levelcap",
-                                  "rowdup", "rowrange"])
+@pytest.mark.parametrize("case", ["order", "self", "below", "crossseq", "seqstart", "seqlast", "noseq", "forkcap",
+                                  "levelcap", "rowdup", "rowrange"])
 @pytest.mark.parametrize("long", [False, True])
 def test_plan_errors_match(case, long):
     """Short streams are planned by one workgroup, long ones by six launches:
@@ -96,6 +96,9 @@ def test_plan_errors_match(case, long):
         seq[2] = seq[1] - 1
     elif case == "seqlast":
         seq[-1] = T - 1
+    elif case == "noseq":  # no sequence at all, but T > 0 tokens
+        seq = np.zeros(1, np.int32)
+        kw = {"max_forks": 0, "max_levels": 1}
     elif case == "forkcap":
         ref = P.plan(parent, seq)
         kw = {"max_forks": max(0, ref["n_fork"] - 1), "max_levels": 64}

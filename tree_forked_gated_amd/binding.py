@@ -59,8 +59,8 @@ class Layout(ctypes.Structure):
 
 
 EXPORTS = ["gdn_tree_workspace_size", "gdn_tree_plan_layout", "gdn_tree_commit_workspace_size", "gdn_tree_plan",
-           "gdn_tree_forward", "gdn_tree_commit", "gdn_tree_check_error", "gdn_tree_strerror",
-           "gdn_tree_last_error", "gdn_tree_version"]
+           "gdn_tree_forward", "gdn_tree_commit", "gdn_tree_check_error",
+           "gdn_tree_strerror", "gdn_tree_last_error", "gdn_tree_version"]
 
 
 def _load():
@@ -119,11 +119,16 @@ def _dtype_code(dt: torch.dtype) -> int:
 # ----------------------------------------------------------------- capacities
 
 def capacities(parent, seq_start) -> dict:
-    """Exact fork-slot and level counts of a tree (host-side, from the same
-    segment rules the device planner applies). A convenience for callers that
-    hold the structure on the host; it synchronises if given device tensors."""
-    parent = np.asarray(parent.cpu() if isinstance(parent, torch.Tensor) else parent, dtype=np.int64)
-    seq_start = np.asarray(seq_start.cpu() if isinstance(seq_start, torch.Tensor) else seq_start, dtype=np.int64)
+    """Exact fork-slot and level counts of a tree whose structure is held on
+    the host (numpy arrays or CPU tensors), from the same segment rules the
+    device planner applies. An explicit utility: forward() never calls it, and
+    it refuses device tensors rather than copy them back."""
+    for x in (parent, seq_start):
+        if isinstance(x, torch.Tensor) and x.device.type != "cpu":
+            raise GdnError("capacities() takes a structure held on the host; pass the capacities of the "
+                           "bucket instead of reading a device tree back")
+    parent = np.asarray(parent, dtype=np.int64)
+    seq_start = np.asarray(seq_start, dtype=np.int64)
     T = parent.shape[0]
     if T == 0:
         return {"max_forks": 0, "max_levels": 1}
@@ -164,7 +169,8 @@ def alloc_workspace(dims: Dims, device) -> torch.Tensor:
     return torch.empty(workspace_size(dims), dtype=torch.uint8, device=device)
 
 
-def check_error(workspace: torch.Tensor, stream=None):
+def check_error(workspace: Optional[torch.Tensor], stream=None):
+    """(code, index) of a workspace's error word."""
     code = ctypes.c_int32(0)
     index = ctypes.c_int64(0)
     _check(lib.gdn_tree_check_error(_ptr(workspace), _stream(stream), ctypes.byref(code), ctypes.byref(index)),
@@ -204,7 +210,7 @@ def _fwd_args(q, k, v, log_gate, beta, parent_idx, seq_start, init_state, out, o
     a.n_state = int(state_rows.numel()) if state_rows is not None else 0
     a.pseudo_v = _ptr(pseudo_v)
     a.workspace = _ptr(workspace)
-    a.workspace_bytes = int(workspace.numel())
+    a.workspace_bytes = 0 if workspace is None else int(workspace.numel())
     a.dv_tile = int(dv_tile)
     a.flags = int(flags)
     return a
@@ -227,10 +233,17 @@ def forward(q, k, v, log_gate, beta, parent_idx, seq_start, init_state=None, *, 
     parent_idx [T] and seq_start [n_seq+1] int32; init_state [n_seq,H,Dv,Dk]
     float32 or None. Returns out rows (all tokens unless out_rows), states of
     state_rows, pseudo-values when keep_pseudo, and the workspace (metadata and
-    error word). max_forks / max_levels default to the tree's exact counts,
-    computed on the host (a synchronising convenience). planned=True reuses
-    the metadata that an earlier call built in ``workspace`` for the same
-    structure (GDN_FWD_PLANNED): only the walk runs."""
+    error word).
+
+    max_forks and max_levels are the fork-slot and level capacities (Flide's
+    fixed capacities per graph bucket, section 3.3.2); they are required. A
+    tree that needs more raises a device error (see ``check``); nothing of the
+    tree is read back to the host. planned=True reuses the metadata that an
+    earlier call built in ``workspace`` for the same structure
+    (GDN_FWD_PLANNED): only the walk runs."""
+    if max_forks is None or max_levels is None:
+        raise GdnError("forward() needs max_forks and max_levels (the bucket's capacities); "
+                       "capacities() gives exact ones for a structure held on the host")
     device = q.device
     T, H, Dk = q.shape
     Dv = v.shape[2]
@@ -239,10 +252,6 @@ def forward(q, k, v, log_gate, beta, parent_idx, seq_start, init_state=None, *, 
     out_rows = _i32(out_rows, device)
     state_rows = _i32(state_rows, device)
     n_seq = seq_start.numel() - 1
-    if max_forks is None or max_levels is None:
-        cap = capacities(parent_idx, seq_start)
-        max_forks = cap["max_forks"] if max_forks is None else max_forks
-        max_levels = cap["max_levels"] if max_levels is None else max_levels
     dims = make_dims(T, H, Dk, Dv, n_seq, _dtype_code(q.dtype), max_forks, max(1, max_levels))
     if workspace is None:
         workspace = alloc_workspace(dims, device)
@@ -264,20 +273,25 @@ def forward(q, k, v, log_gate, beta, parent_idx, seq_start, init_state=None, *, 
 
 def plan(parent_idx, seq_start, *, T=None, H=1, Dk=16, Dv=16, dtype_code=GDN_F32, out_rows=None, state_rows=None,
          max_forks=None, max_levels=None, device="cuda", stream=None) -> dict:
-    """Run only the metadata kernels and return every table (host numpy)."""
+    """Run only the metadata kernels and return every table (host numpy; an
+    inspection utility that synchronises). Without capacities the structure
+    must be given on the host, and its exact counts are used."""
+    if max_forks is None or max_levels is None:
+        try:
+            cap = capacities(parent_idx, seq_start)
+        except GdnError:
+            raise
+        except Exception:  # malformed structure: any capacity will do, the device reports the error
+            n = int(np.asarray(parent_idx).shape[0])
+            cap = {"max_forks": n, "max_levels": 8}
+        max_forks = cap["max_forks"] if max_forks is None else max_forks
+        max_levels = cap["max_levels"] if max_levels is None else max_levels
     parent_idx = _i32(parent_idx, device)
     seq_start = _i32(seq_start, device)
     out_rows = _i32(out_rows, device)
     state_rows = _i32(state_rows, device)
     T = parent_idx.numel() if T is None else T
     n_seq = seq_start.numel() - 1
-    if max_forks is None or max_levels is None:
-        try:
-            cap = capacities(parent_idx, seq_start)
-        except Exception:  # malformed structure: any capacity will do, the device reports the error
-            cap = {"max_forks": T, "max_levels": 8}
-        max_forks = cap["max_forks"] if max_forks is None else max_forks
-        max_levels = cap["max_levels"] if max_levels is None else max_levels
     dims = make_dims(T, H, Dk, Dv, n_seq, dtype_code, max_forks, max(1, max_levels))
     ws = alloc_workspace(dims, device)
     a = FwdArgs()

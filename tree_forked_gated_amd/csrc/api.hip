@@ -3,11 +3,87 @@
 // gdn_tree_check_error), no state kept between calls.
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "gdn_internal.h"
 
 using namespace gdn;
+
+namespace gdn {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];  // 0 = not queried yet
+// (kernel, device) pairs whose dynamic-LDS attribute is set, with the
+// kernel's occupancy at that size: a small open-addressed table
+constexpr int kLdsSlots = 256;
+std::atomic<const void*> g_lds_kern[kLdsSlots];
+std::atomic<int> g_lds_dev[kLdsSlots];
+std::atomic<int> g_lds_bytes[kLdsSlots];
+std::atomic<int> g_lds_occ[kLdsSlots];
+}  // namespace
+
+hipError_t current_device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int v = (dev >= 0 && dev < kMaxDevices) ? g_cus[dev].load(std::memory_order_relaxed) : 0;
+  if (v <= 0) {
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(v, std::memory_order_relaxed);
+  }
+  *cus = v;
+  return hipSuccess;
+}
+
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes, int threads, int* occupancy) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  auto query = [&](int* occ) -> hipError_t {
+    hipError_t r = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (r != hipSuccess) return r;
+    *occ = 1;
+    r = hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, kernel, threads, bytes);
+    if (r != hipSuccess) return r;
+    if (*occ < 1) *occ = 1;
+    return hipSuccess;
+  };
+  const size_t h0 = ((reinterpret_cast<uintptr_t>(kernel) >> 4) * 31u + (unsigned)dev) % kLdsSlots;
+  for (size_t i = 0; i < kLdsSlots; ++i) {
+    const size_t j = (h0 + i) % kLdsSlots;
+    const void* k = g_lds_kern[j].load(std::memory_order_acquire);
+    if (k == kernel && g_lds_dev[j].load(std::memory_order_acquire) == dev &&
+        g_lds_bytes[j].load(std::memory_order_acquire) == bytes) {
+      const int occ = g_lds_occ[j].load(std::memory_order_acquire);
+      if (occ > 0) {
+        if (occupancy) *occupancy = occ;
+        return hipSuccess;
+      }
+    }
+    if (k == nullptr) {
+      int occ = 1;
+      e = query(&occ);
+      if (e != hipSuccess) return e;
+      if (occupancy) *occupancy = occ;
+      const void* expect = nullptr;
+      if (g_lds_kern[j].compare_exchange_strong(expect, kernel, std::memory_order_acq_rel)) {
+        g_lds_dev[j].store(dev, std::memory_order_release);
+        g_lds_bytes[j].store(bytes, std::memory_order_release);
+        g_lds_occ[j].store(occ, std::memory_order_release);
+      }
+      return hipSuccess;
+    }
+  }
+  int occ = 1;  // table full: query on every call
+  e = query(&occ);
+  if (occupancy) *occupancy = occ;
+  return e;
+}
+
+}  // namespace gdn
 
 namespace {
 
@@ -34,6 +110,8 @@ int check_dims(const gdn_tree_dims* d) {
   const bool dk_ok = d->dtype == GDN_BF16 ? (d->Dk == 32 || d->Dk == 64 || d->Dk == 128)
                                           : (d->Dk == 16 || d->Dk == 32 || d->Dk == 64);
   if (!dk_ok) return fail(GDN_ERR_DIMS, "Dk must be 32, 64 or 128 (bf16) or 16, 32 or 64 (fp32)");
+  if ((long long)d->H * (d->Dk > d->Dv ? d->Dk : d->Dv) >= (1ll << 24))
+    return fail(GDN_ERR_DIMS, "H * max(Dk, Dv) must stay below 2^24");
   if (d->max_forks < 0 || d->max_levels < 1 || d->max_levels > 4096)
     return fail(GDN_ERR_DIMS, "max_forks must be >= 0 and max_levels in [1, 4096]");
   return GDN_OK;
@@ -41,11 +119,8 @@ int check_dims(const gdn_tree_dims* d) {
 
 // Columns of Dv per workgroup: enough items to give every CU one, widest tile otherwise.
 int choose_dv_tile(const gdn_tree_dims& d) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-  }
+  int cus = 256, v = 0;
+  if (current_device_cus(&v) == hipSuccess && v > 0) cus = v;
   const long long units = (long long)(d.n_seq > 0 ? d.n_seq : 1) * d.H;
   const int max_bv = d.dtype == GDN_BF16 ? 64 : 32;
   for (int bv = max_bv; bv >= 16; bv >>= 1) {
@@ -88,6 +163,8 @@ int check_fwd(const gdn_tree_fwd_args* a, bool walk, LayoutFull* L) {
 }
 
 }  // namespace
+
+static int forward_impl(const gdn_tree_fwd_args* a, void* stream);
 
 extern "C" {
 
@@ -149,7 +226,9 @@ int gdn_tree_plan(const gdn_tree_fwd_args* a, void* stream) {
   return GDN_OK;
 }
 
-int gdn_tree_forward(const gdn_tree_fwd_args* a, void* stream) {
+int gdn_tree_forward(const gdn_tree_fwd_args* a, void* stream) { return forward_impl(a, stream); }
+
+static int forward_impl(const gdn_tree_fwd_args* a, void* stream) {
   LayoutFull L;
   int rc = check_fwd(a, true, &L);
   if (rc) return rc;
@@ -177,9 +256,11 @@ int gdn_tree_commit(const gdn_tree_commit_args* a, void* stream) {
   if (!a->workspace) return fail(GDN_ERR_NULL, "workspace is NULL");
   if (a->workspace_bytes < gdn_tree_commit_workspace_size()) return fail(GDN_ERR_WORKSPACE, "commit workspace too small");
   if (a->n_path > 0) {
-    if (!a->k || !a->log_gate || !a->parent_idx || !a->seq_start || !a->pseudo_v || !a->path_ptr || !a->path_seq ||
-        !a->out_state)
-      return fail(GDN_ERR_NULL, "k, log_gate, parent_idx, seq_start, pseudo_v, path_ptr, path_seq and out_state are required");
+    if (!a->k || !a->log_gate || !a->parent_idx || !a->seq_start || !a->pseudo_v || !a->path_ptr ||
+        !a->path_nodes || !a->path_seq || !a->out_state)
+      return fail(GDN_ERR_NULL,
+                  "k, log_gate, parent_idx, seq_start, pseudo_v, path_ptr, path_nodes, path_seq and out_state are "
+                  "required when n_path > 0");
     if (!aligned16(a->out_state) || (a->init_state && !aligned16(a->init_state)))
       return fail(GDN_ERR_ARGS, "states must be 16-byte aligned");
   }

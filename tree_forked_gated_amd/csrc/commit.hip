@@ -33,7 +33,9 @@ struct CommitArgs {
   const int* path_seq;
   float* out;
   unsigned long long* err;
-  int H, Dk, Dv, n_seq;
+  int H, Dk, Dv, n_seq, T;
+  int n_path;
+  int own_err;  // 1: workgroup (0, 0, 0) checks every path and stores the error word itself
 };
 
 template <typename E>
@@ -41,6 +43,38 @@ __device__ inline float upc(E x) { return (float)x; }
 
 __global__ void k_reset(unsigned long long* err) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *err = kNoError;
+}
+
+// Is path p a parent chain from a root of its sequence down to its last node?
+// Every index is checked before it is used.
+__device__ inline bool path_ok(const CommitArgs& a, int p) {
+  const int seq = a.path_seq[p];
+  const int beg = a.path_ptr[p], end = a.path_ptr[p + 1];
+  if (seq < 0 || seq >= a.n_seq || end < beg) return false;
+  if (end == beg) return true;
+  const int s_0 = a.seq_start[seq], s_1 = a.seq_start[seq + 1];
+  if (s_0 < 0 || s_1 > a.T || s_1 <= s_0) return false;
+  for (int j = beg; j < end; ++j) {
+    const int t = a.path_nodes[j];
+    const int want = (j == beg) ? -1 : a.path_nodes[j - 1];
+    if (t < s_0 || t >= s_1 || a.parent[t] != want) return false;
+  }
+  return true;
+}
+
+// The error word of a call with few paths: the smallest bad path, found by one
+// workgroup (one path per thread at a time) and stored without atomics, so the
+// word needs no reset before the call.
+__device__ inline void check_all_paths(const CommitArgs& a) {
+  __shared__ int s_first;
+  if (threadIdx.x == 0) s_first = 0x7fffffff;
+  __syncthreads();
+  for (int p = threadIdx.x; p < a.n_path; p += blockDim.x)
+    if (!path_ok(a, p)) atomicMin(&s_first, p);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *a.err = s_first == 0x7fffffff ? kNoError
+                                   : (((unsigned long long)(unsigned)GDN_DEV_PATH << 32) | (unsigned)s_first);
 }
 
 // One workgroup per (path, head, 32 rows of S). The rows of S_0 are loaded
@@ -80,9 +114,10 @@ __global__ void __launch_bounds__(kThreads, 6) k_commit(CommitArgs a) {
   }
   const E* kg = reinterpret_cast<const E*>(a.k);
   const E* gg = reinterpret_cast<const E*>(a.g);
-  const int s_0 = bad_path ? 0 : a.seq_start[seq], s_1 = bad_path ? 0 : a.seq_start[seq + 1];
-  // a non-empty path needs a non-empty sequence; nothing is loaded otherwise
-  const bool no_tokens = !bad_path && end > beg && s_1 <= s_0;
+  int s_0 = bad_path ? 0 : a.seq_start[seq], s_1 = bad_path ? 0 : a.seq_start[seq + 1];
+  // a non-empty path needs a non-empty sequence inside [0, T); nothing is loaded otherwise
+  const bool no_tokens = !bad_path && end > beg && (s_1 <= s_0 || s_0 < 0 || s_1 > a.T);
+  if (no_tokens) s_0 = s_1 = 0;
   bad |= no_tokens;
   float4 acc[kPer4];
 #pragma unroll
@@ -140,8 +175,9 @@ __global__ void __launch_bounds__(kThreads, 6) k_commit(CommitArgs a) {
     }
     __syncthreads();
   }
+  if (a.own_err && p == 0 && h == 0 && vb == 0) check_all_paths(a);
   if (__syncthreads_or(bad)) {
-    if (tid == 0) raise_error(a.err, GDN_DEV_PATH, p);
+    if (tid == 0 && !a.own_err) raise_error(a.err, GDN_DEV_PATH, p);
     return;
   }
   const float ga = __expf(sSigma);
@@ -181,7 +217,13 @@ hipError_t launch_commit(const gdn_tree_commit_args& c, unsigned long long* err,
   a.Dk = c.dims.Dk;
   a.Dv = c.dims.Dv;
   a.n_seq = c.dims.n_seq;
-  hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, s, err);
+  a.T = (int)c.dims.T;
+  a.n_path = c.n_path;
+  // With up to kOwnErrPaths paths one workgroup of the commit decides the error
+  // word by itself; otherwise the word is reset first and raised by atomics.
+  constexpr int kOwnErrPaths = 1024;
+  a.own_err = c.n_path > 0 && c.n_path <= kOwnErrPaths;
+  if (!a.own_err) hipLaunchKernelGGL(k_reset, dim3(1), dim3(64), 0, s, err);
   if (c.n_path > 0) {
     dim3 grid(c.n_path, c.dims.H, (c.dims.Dv + kRows - 1) / kRows);
     if (c.dims.dtype == GDN_BF16) hipLaunchKernelGGL(k_commit<__bf16>, grid, dim3(256), 0, s, a);

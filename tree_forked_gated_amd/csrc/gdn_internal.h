@@ -71,6 +71,13 @@ struct LayoutFull {
 bool compute_layout(const gdn_tree_dims& d, LayoutFull* L);
 Meta meta_from(void* workspace, const LayoutFull& L);
 
+// Per-process caches of device queries (host): the compute-unit count of the
+// current device, and the dynamic-LDS attribute of a kernel, set once per
+// (kernel, device), with its occupancy at `threads` threads when asked for
+// (occupancy may be NULL). Thread safe; a race only repeats idempotent calls.
+hipError_t current_device_cus(int* cus);
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes, int threads, int* occupancy);
+
 // Host launchers (enqueue only). Return hipSuccess or the launch error.
 hipError_t launch_plan(const gdn_tree_fwd_args& a, const Meta& m, const LayoutFull& L, unsigned long long tag,
                        hipStream_t s);
@@ -85,7 +92,6 @@ bool walk_supported(int dtype, int dk, int bv);
 // Pipelined MFMA walk for bf16 inputs with d_k = 128 (d_v tiles of 16, 32 or 64
 // columns): state waves plus helper waves
 bool walk_pipe_supported(int dtype, int dk, int bv);
-bool walk_pipe_fits(const gdn_tree_dims& d);  // sizes within its 32-bit offsets
 hipError_t launch_walk_pipe(const gdn_tree_fwd_args& a, const Meta& m, int bv, hipStream_t s);
 int walk_lds_bytes(int dtype, int dk, int bv);
 

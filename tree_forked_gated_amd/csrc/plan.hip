@@ -49,6 +49,7 @@ __device__ inline bool bad_csr(const Meta& m) { return (*m.err >> 32) == (unsign
 __global__ void k_init(Meta m, int T, int n_seq, int max_levels) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < T) {
+    m.tok_seq[i] = 0;
     m.out_map[i] = kUnmapped;
     m.state_map[i] = kUnmapped;
     m.is_fork[i] = 0;
@@ -100,9 +101,10 @@ __global__ void k_tokens(const int* parent, const int* seq_start, int n_seq, int
   if (gid <= n_seq) {
     const int s = (int)gid;
     const int v = seq_start[s];
-    if (s == 0) {
-      if (v != 0) raise_error(m.err, GDN_DEV_SEQ_START, 0);
-    } else if (v < seq_start[s - 1] || v > T) {
+    // the last entry must be T also when it is the first (n_seq = 0)
+    if (s == 0 && v != 0) {
+      raise_error(m.err, GDN_DEV_SEQ_START, 0);
+    } else if (s > 0 && (v < seq_start[s - 1] || v > T)) {
       raise_error(m.err, GDN_DEV_SEQ_START, s);
     } else if (s == n_seq && v != T) {
       raise_error(m.err, GDN_DEV_SEQ_START, s);
@@ -463,6 +465,7 @@ __global__ void __launch_bounds__(kPT) k_plan_small(const int* parent, const int
     for (int i = tid; i <= n_seq; i += kPT) s_ss[i] = seq_start[i];
   // -- clear (as k_init)
   for (int i = tid; i < T; i += kPT) {
+    m.tok_seq[i] = 0;
     m.out_map[i] = kUnmapped;
     m.state_map[i] = kUnmapped;
     m.is_fork[i] = 0;
@@ -487,9 +490,9 @@ __global__ void __launch_bounds__(kPT) k_plan_small(const int* parent, const int
   // -- sequence checks, row maps, per-token checks, segment starts and fork flags (as k_tokens)
   for (int s = tid; s <= n_seq; s += kPT) {
     const int v = ss[s];
-    if (s == 0) {
-      if (v != 0) raise_error(m.err, GDN_DEV_SEQ_START, 0);
-    } else if (v < ss[s - 1] || v > T) {
+    if (s == 0 && v != 0) {
+      raise_error(m.err, GDN_DEV_SEQ_START, 0);
+    } else if (s > 0 && (v < ss[s - 1] || v > T)) {
       raise_error(m.err, GDN_DEV_SEQ_START, s);
     } else if (s == n_seq && v != T) {
       raise_error(m.err, GDN_DEV_SEQ_START, s);

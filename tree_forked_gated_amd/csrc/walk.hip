@@ -501,17 +501,11 @@ template <typename E, int DK, int BV>
 hipError_t run(const WalkArgs& wa, int levels, hipStream_t s) {
   auto kern = k_walk<E, DK, BV>;
   constexpr int bytes = Cfg<E, DK, BV>::bytes;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     bytes);
+  int cus = 0, occ = 1;
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), bytes, kThreads, &occ);
   if (e != hipSuccess) return e;
-  int dev = 0, cus = 0, occ = 0;
-  e = hipGetDevice(&dev);
+  e = current_device_cus(&cus);
   if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kThreads, bytes);
-  if (e != hipSuccess) return e;
-  if (occ < 1) occ = 1;
   const int grid = cus * occ;
   for (int l = 0; l < levels; ++l) {
     WalkArgs x = wa;
@@ -546,7 +540,7 @@ int walk_lds_bytes(int dtype, int dk, int bv) {
 }
 
 hipError_t launch_walk(const gdn_tree_fwd_args& fa, const Meta& m, int bv, hipStream_t s) {
-  if (walk_pipe_supported(fa.dims.dtype, fa.dims.Dk, bv) && walk_pipe_fits(fa.dims)) return launch_walk_pipe(fa, m, bv, s);
+  if (walk_pipe_supported(fa.dims.dtype, fa.dims.Dk, bv)) return launch_walk_pipe(fa, m, bv, s);
   WalkArgs wa;
   wa.q = fa.q;
   wa.k = fa.k;

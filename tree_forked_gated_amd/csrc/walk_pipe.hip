@@ -928,23 +928,25 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
         for (int nb = 0; nb < NB; ++nb) O[nb][rb] = mma32(cat8b(Vb[nb][2 * mp], Vb[nb][2 * mp + 1]), pb, O[nb][rb]);
       }
     }
-    // lane (l16, g4) holds columns 4 g4 .. 4 g4 + 3 of block nb for token 16 rb + l16
+    // lane (l16, g4) holds columns 4 g4 .. 4 g4 + 3 of block nb for token 16 rb + l16.
+    // Row offsets are 64-bit at the chunk (or row) base and 32-bit inside a chunk.
     const unsigned ccol = (unsigned)h * a.Dv + (unsigned)(v0w + 4 * g4);
     if (a.out_all && n == kChunk) {  // every token of a full chunk is an output row, in stream order
+      __bf16* oc = a.out + (size_t)t0 * HDv;
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          *reinterpret_cast<bf16x4*>(a.out + ((unsigned)t0 + 16 * rb + l16) * HDv + ccol + 16 * nb) = to_bf4(O[nb][rb]);
+          *reinterpret_cast<bf16x4*>(oc + (unsigned)(16 * rb + l16) * HDv + ccol + 16 * nb) = to_bf4(O[nb][rb]);
     } else {
       const int* sOR = reinterpret_cast<const int*>(tb + tOR);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const int orow = sOR[16 * rb + l16];
         if (orow >= 0) {
+          __bf16* orp = a.out + (size_t)orow * HDv + ccol;
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            *reinterpret_cast<bf16x4*>(a.out + (unsigned)orow * HDv + ccol + 16 * nb) = to_bf4(O[nb][rb]);
+          for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<bf16x4*>(orp + 16 * nb) = to_bf4(O[nb][rb]);
         }
       }
     }
@@ -953,7 +955,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
   if (a.pv) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float* pvb = a.pv + ((unsigned)t0 + 4 * g4) * HDv + (unsigned)h * a.Dv + (unsigned)(v0w + 16 * nb + l16);
+      float* pvb = a.pv + (size_t)t0 * HDv + (unsigned)(4 * g4) * HDv + (unsigned)h * a.Dv + (unsigned)(v0w + 16 * nb + l16);
       if (n == kChunk) {
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
@@ -1191,13 +1193,10 @@ template <int BV>
 hipError_t run(const Args& wa, int levels, hipStream_t s) {
   auto kern = k_walk_pipe<BV>;
   constexpr int bytes = Cfg<BV>::bytes;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     bytes);
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), bytes, Cfg<BV>::NTHR, nullptr);
   if (e != hipSuccess) return e;
-  int dev = 0, cus = 0;
-  e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  e = current_device_cus(&cus);
   if (e != hipSuccess) return e;
   // one workgroup per CU (bounded by LDS), persistent over the level's items;
   // a multiple of the XCD count so that every XCD has the same number of workgroups
@@ -1214,12 +1213,6 @@ hipError_t run(const Args& wa, int levels, hipStream_t s) {
 
 bool walk_pipe_supported(int dtype, int dk, int bv) {
   return dtype == GDN_BF16 && dk == DK && (bv == 16 || bv == 32 || bv == 64);
-}
-
-bool walk_pipe_fits(const gdn_tree_dims& d) {
-  // the kernel addresses q, k, v, out and pseudo_v with 32-bit element offsets
-  const long long per_token = (long long)d.H * (d.Dk > d.Dv ? d.Dk : d.Dv);
-  return d.T * per_token < (1ll << 30);
 }
 
 hipError_t launch_walk_pipe(const gdn_tree_fwd_args& fa, const Meta& m, int bv, hipStream_t s) {

@@ -37,9 +37,16 @@ CHUNK = 64  # documented here only to size workloads; the kernels own their tili
 def bf16_round(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to the nearest bf16 (ties to even); returns fp32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).reshape(x.shape)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("bf16_round expects finite values")
+    u = x.view(np.uint32)
+    # finite values stay below 0xFF800000 after the rounding increment, so
+    # 32-bit arithmetic cannot wrap
+    r = (u >> 16) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32).reshape(x.shape)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -116,16 +123,28 @@ def root_path(parent: np.ndarray, node: int) -> List[int]:
     return out[::-1]
 
 
+def _normal_f32(rng, shape, unit_rows=False, rows_per_block=2048):
+    """Standard normal fp64 draws in C order, cast to fp32 (and L2-normalised
+    along the last axis in fp32 when unit_rows). Drawn block by block along the
+    first axis: the generator yields the same numbers in the same order as one
+    draw of the whole shape, without a multi-gigabyte fp64 temporary."""
+    out = np.empty(shape, dtype=np.float32)
+    n = shape[0] if len(shape) else 0
+    for a in range(0, n, rows_per_block):
+        b = min(n, a + rows_per_block)
+        blk = rng.standard_normal((b - a,) + tuple(shape[1:])).astype(np.float32)
+        if unit_rows:
+            nrm = np.sqrt(np.sum(blk * blk, axis=-1, keepdims=True, dtype=np.float32), dtype=np.float32)
+            blk = (blk / nrm).astype(np.float32)
+        out[a:b] = blk
+    return out
+
+
 def _values(rng, T, H, Dk, Dv, dtype):
     """Draw q, k, v, beta, log_gate in the documented order and recipe."""
-    def unit_rows(a):
-        a = a.astype(np.float32)
-        n = np.sqrt(np.sum(a * a, axis=-1, keepdims=True, dtype=np.float32), dtype=np.float32)
-        return (a / n).astype(np.float32)
-
-    q = unit_rows(rng.standard_normal((T, H, Dk)))
-    k = unit_rows(rng.standard_normal((T, H, Dk)))
-    v = rng.standard_normal((T, H, Dv)).astype(np.float32)
+    q = _normal_f32(rng, (T, H, Dk), unit_rows=True)
+    k = _normal_f32(rng, (T, H, Dk), unit_rows=True)
+    v = _normal_f32(rng, (T, H, Dv))
     xb = rng.standard_normal((T, H))
     beta = (1.0 / (1.0 + np.exp(-xb))).astype(np.float32)
     xg = rng.standard_normal((T, H))
