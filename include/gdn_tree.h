@@ -253,11 +253,36 @@ int gdn_tree_plan(const gdn_tree_fwd_args* a, void* stream);
  */
 int gdn_tree_forward(const gdn_tree_fwd_args* a, void* stream);
 
+/*
+ * gdn_tree_forward without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. The workspace is a static device array of
+ * GDN_TREE_STATIC_WORKSPACE_BYTES bytes inside the library, one per GPU, held
+ * from the library's first use on that GPU until the process ends. a->workspace
+ * and a->workspace_bytes are ignored; everything else is as for
+ * gdn_tree_forward (inputs and outputs are still the caller's).
+ *  - Sizes whose workspace (gdn_tree_workspace_size) exceeds the array are
+ *    rejected with GDN_ERR_WORKSPACE and a message; nothing is enqueued.
+ *  - The call allocates nothing (no hipMalloc, no library allocation). The
+ *    device address of the array is looked up once per device, on the first
+ *    call with that device current.
+ *  - Every call on a GPU shares that GPU's array, which keeps the last call's
+ *    metadata and fork states: calls that overlap on one GPU (other streams,
+ *    other threads) race and must be serialised by the caller. The metadata
+ *    kernels rebuild everything a walk reads, so nothing needs clearing between
+ *    calls; GDN_FWD_PLANNED reuses the array's last plan.
+ *  - gdn_tree_check_error(NULL, stream, ...) reads the array's error word on the
+ *    current device.
+ */
+#define GDN_TREE_STATIC_WORKSPACE_BYTES (64u << 20)
+int gdn_tree_forward_static(const gdn_tree_fwd_args* a, void* stream);
+
 /* Rebuilds the state after each accepted path's last node (TreeWY Eq. 3). */
 int gdn_tree_commit(const gdn_tree_commit_args* a, void* stream);
 
 /* Synchronises `stream`, then reads the workspace's error word. *code gets a
- * gdn_dev_error, *index its index (0 when there is no error). */
+ * gdn_dev_error, *index its index (0 when there is no error). workspace NULL:
+ * the static workspace of gdn_tree_forward_static on the current device. */
 int gdn_tree_check_error(const void* workspace, void* stream, int32_t* code, int64_t* index);
 
 /* Static text for a gdn_status or, shifted by 100 (100 + code), a gdn_dev_error. */

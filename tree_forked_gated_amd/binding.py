@@ -59,8 +59,9 @@ class Layout(ctypes.Structure):
 
 
 EXPORTS = ["gdn_tree_workspace_size", "gdn_tree_plan_layout", "gdn_tree_commit_workspace_size", "gdn_tree_plan",
-           "gdn_tree_forward", "gdn_tree_commit", "gdn_tree_check_error",
+           "gdn_tree_forward", "gdn_tree_forward_static", "gdn_tree_commit", "gdn_tree_check_error",
            "gdn_tree_strerror", "gdn_tree_last_error", "gdn_tree_version"]
+STATIC_WORKSPACE_BYTES = 64 << 20  # gdn_tree.h GDN_TREE_STATIC_WORKSPACE_BYTES
 
 
 def _load():
@@ -74,7 +75,7 @@ def _load():
     lib.gdn_tree_last_error.restype = ctypes.c_char_p
     lib.gdn_tree_commit_workspace_size.restype = ctypes.c_size_t
     for name in ["gdn_tree_workspace_size", "gdn_tree_plan_layout", "gdn_tree_plan", "gdn_tree_forward",
-                 "gdn_tree_commit", "gdn_tree_check_error", "gdn_tree_version"]:
+                 "gdn_tree_forward_static", "gdn_tree_commit", "gdn_tree_check_error", "gdn_tree_version"]:
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -170,7 +171,8 @@ def alloc_workspace(dims: Dims, device) -> torch.Tensor:
 
 
 def check_error(workspace: Optional[torch.Tensor], stream=None):
-    """(code, index) of a workspace's error word."""
+    """(code, index) of a workspace's error word; None reads the static
+    workspace of forward_static on the current device."""
     code = ctypes.c_int32(0)
     index = ctypes.c_int64(0)
     _check(lib.gdn_tree_check_error(_ptr(workspace), _stream(stream), ctypes.byref(code), ctypes.byref(index)),
@@ -269,6 +271,22 @@ def forward(q, k, v, log_gate, beta, parent_idx, seq_start, init_state=None, *, 
     if check:
         raise_device_error(workspace, stream)
     return ForwardResult(out, state_out, pseudo_v, workspace)
+
+
+def forward_static(q, k, v, log_gate, beta, parent_idx, seq_start, init_state, *, out, max_forks, max_levels,
+                   out_rows=None, state_rows=None, state_out=None, pseudo_v=None, dv_tile=0, stream=None,
+                   planned=False) -> None:
+    """gdn_tree_forward_static: the forward with the library's static device
+    workspace instead of a caller buffer. Every output buffer is the
+    caller's (this wrapper allocates nothing either); errors are read with
+    check_error(None)."""
+    T, H, Dk = q.shape
+    Dv = v.shape[2]
+    n_seq = seq_start.numel() - 1
+    dims = make_dims(T, H, Dk, Dv, n_seq, _dtype_code(q.dtype), max_forks, max(1, max_levels))
+    a = _fwd_args(q, k, v, log_gate, beta, parent_idx, seq_start, init_state, out, out_rows, state_out, state_rows,
+                  pseudo_v, None, dims, dv_tile, FWD_PLANNED if planned else 0)
+    _check(lib.gdn_tree_forward_static(ctypes.byref(a), _stream(stream)), "gdn_tree_forward_static")
 
 
 def plan(parent_idx, seq_start, *, T=None, H=1, Dk=16, Dv=16, dtype_code=GDN_F32, out_rows=None, state_rows=None,

@@ -10,6 +10,11 @@
 
 using namespace gdn;
 
+// Workspace of gdn_tree_forward_static: one copy per GPU, held until the
+// process ends. Host code never uses this name as an address: the device
+// address of each GPU's copy is looked up once per device (static_workspace).
+static __device__ __align__(256) unsigned char scratch[GDN_TREE_STATIC_WORKSPACE_BYTES];
+
 namespace gdn {
 
 namespace {
@@ -81,6 +86,28 @@ hipError_t ensure_dynamic_lds(const void* kernel, int bytes, int threads, int* o
   e = query(&occ);
   if (occupancy) *occupancy = occ;
   return e;
+}
+
+namespace {
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+}  // namespace
+
+// Device address of the static workspace on the current device (looked up on
+// the first call on each device, with that device current).
+hipError_t static_workspace(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace gdn
@@ -228,6 +255,29 @@ int gdn_tree_plan(const gdn_tree_fwd_args* a, void* stream) {
 
 int gdn_tree_forward(const gdn_tree_fwd_args* a, void* stream) { return forward_impl(a, stream); }
 
+int gdn_tree_forward_static(const gdn_tree_fwd_args* a, void* stream) {
+  if (!a) return fail(GDN_ERR_NULL, "args is NULL");
+  int rc = check_dims(&a->dims);
+  if (rc) return rc;
+  LayoutFull L;
+  if (!compute_layout(a->dims, &L)) return fail(GDN_ERR_DIMS, "bad sizes");
+  if (L.pub.total > (size_t)GDN_TREE_STATIC_WORKSPACE_BYTES) {
+    char msg[200];
+    snprintf(msg, sizeof msg,
+             "these sizes need a %zu-byte workspace, more than the %zu bytes of the static workspace of "
+             "gdn_tree_forward_static; use gdn_tree_forward with a workspace of its own",
+             L.pub.total, (size_t)GDN_TREE_STATIC_WORKSPACE_BYTES);
+    return fail(GDN_ERR_WORKSPACE, msg);
+  }
+  void* ws = nullptr;
+  hipError_t e = static_workspace(&ws);
+  if (e != hipSuccess) return fail_hip(e, "gdn_tree_forward_static (static workspace address)");
+  gdn_tree_fwd_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = (size_t)GDN_TREE_STATIC_WORKSPACE_BYTES;
+  return forward_impl(&b, stream);
+}
+
 static int forward_impl(const gdn_tree_fwd_args* a, void* stream) {
   LayoutFull L;
   int rc = check_fwd(a, true, &L);
@@ -270,7 +320,13 @@ int gdn_tree_commit(const gdn_tree_commit_args* a, void* stream) {
 }
 
 int gdn_tree_check_error(const void* workspace, void* stream, int32_t* code, int64_t* index) {
-  if (!workspace || !code || !index) return fail(GDN_ERR_NULL, "workspace, code and index are required");
+  if (!code || !index) return fail(GDN_ERR_NULL, "code and index are required");
+  if (!workspace) {  // the static workspace of gdn_tree_forward_static on the current device
+    void* ws = nullptr;
+    hipError_t e = static_workspace(&ws);
+    if (e != hipSuccess) return fail_hip(e, "gdn_tree_check_error (static workspace address)");
+    workspace = ws;
+  }
   unsigned long long word = 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, s);
