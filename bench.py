@@ -317,7 +317,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(walk_tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(walk_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
     roof.update({"kernel": "k_walk_pipe" if wl.dtype == "bf16" and wl.Dk == 128 else "k_walk",
-                 "unit": "one forward's walk: every level launch of a step",
+                 "launch_unit": "one forward's walk: every level launch of a step",
                  "launches_per_step": cap["max_levels"], "ms_per_step": round(ms_walk, 5),
                  "alg_bytes": cnt["bytes"], "alg_flops": cnt["flops"],
                  "mfma_frac": round(walk_tflops / BF16_PEAK_TFLOPS, 4),
