@@ -206,6 +206,9 @@ def _fwd_args(q, k, v, log_gate, beta, parent_idx, seq_start, init_state, out, o
     a.init_state = _ptr(init_state)
     a.out = _ptr(out) if out is not None and out.numel() > 0 else None
     a.out_rows = _ptr(out_rows)
+    if out_rows is not None and out_rows.numel() == 0:
+        # no readout rows: any valid address (never read) keeps "out_rows given" apart from "every token"
+        a.out_rows = _ptr(parent_idx) if parent_idx is not None and parent_idx.numel() else _ptr(seq_start)
     a.n_out = int(out.shape[0]) if out is not None else 0
     a.state_out = _ptr(state_out) if state_out is not None and state_out.numel() > 0 else None
     a.state_rows = _ptr(state_rows) if state_rows is not None and state_rows.numel() > 0 else None
