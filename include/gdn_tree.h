@@ -280,6 +280,72 @@ int gdn_tree_forward_static(const gdn_tree_fwd_args* a, void* stream);
 /* Rebuilds the state after each accepted path's last node (TreeWY Eq. 3). */
 int gdn_tree_commit(const gdn_tree_commit_args* a, void* stream);
 
+/*
+ * ForkAttention: full attention over the same tree-structured flat stream, for
+ * the full-attention layers of a hybrid model (Flide, "Accelerating Decision
+ * Inference with Exact State Forking", section 3.2.1 "Full-Attention Layers").
+ * Token t attends to its ancestors-or-self in its own sequence (the rule under
+ * which every question computes its standalone prompt, section 3.2.3; the
+ * page's Equation 3 that states it did not survive extraction):
+ *
+ *     o_t = sum over j ancestor-or-self of t of softmax_j(scale * q_t . k_j) v_j
+ *
+ * per query head h, with key/value head h / (Hq / Hkv) (grouped heads).
+ * The key ranges of every 64-token query chunk (its own segment's prefix and
+ * each ancestor segment's prefix up to the fork) are built on the GPU from the
+ * recurrence's segment tables (section 3.3.1); fully visible key tiles take no
+ * mask. Launch shapes depend only on the sizes.
+ *
+ * Sizes: T tokens (< 2^31), Hq query heads, Hkv key/value heads (Hq a multiple
+ * of Hkv, Hq * D < 2^24), D = 128, dtype GDN_BF16, n_seq sequences, max_levels
+ * the fork-nesting capacity in [1, 64] (a deeper tree raises
+ * GDN_DEV_LEVEL_CAPACITY and nothing is computed).
+ */
+typedef struct gdn_attn_dims {
+  int64_t T;
+  int32_t Hq, Hkv, D;
+  int32_t n_seq;
+  int32_t dtype;
+  int32_t max_levels;
+} gdn_attn_dims;
+
+/* GDN_ATTN_PLANNED: the workspace holds the tables an earlier gdn_tree_attention
+ * built for the same dims, parent_idx and seq_start; only the attention runs
+ * (a model's full-attention layers of one round share them). A workspace
+ * planned for other sizes raises GDN_DEV_NOT_PLANNED. */
+#define GDN_ATTN_PLANNED 1u
+
+/*
+ * Arguments of gdn_tree_attention.
+ *  scale                     softmax scale (commonly 1 / sqrt(D))
+ *  q [T, Hq, D], k and v [T, Hkv, D]   bf16, token-major, 16-byte aligned
+ *  parent_idx [T], seq_start [n_seq + 1]   the stream's structure, as for gdn_tree_forward
+ *  out [T, Hq, D]            bf16, 16-byte aligned
+ *  workspace                 at least gdn_tree_attention_workspace_size bytes, 256-byte aligned;
+ *                            its error word is read with gdn_tree_check_error
+ *  flags                     0 or GDN_ATTN_PLANNED
+ */
+typedef struct gdn_attn_args {
+  gdn_attn_dims dims;
+  float scale;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* parent_idx;
+  const int32_t* seq_start;
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+  uint32_t flags;
+} gdn_attn_args;
+
+/* Workspace bytes of gdn_tree_attention for these sizes. Host only. */
+int gdn_tree_attention_workspace_size(const gdn_attn_dims* dims, size_t* bytes);
+
+/* ForkAttention over the stream: metadata (unless GDN_ATTN_PLANNED), then the
+ * attention kernel. Enqueue only. */
+int gdn_tree_attention(const gdn_attn_args* a, void* stream);
+
 /* Synchronises `stream`, then reads the workspace's error word. *code gets a
  * gdn_dev_error, *index its index (0 when there is no error). workspace NULL:
  * the static workspace of gdn_tree_forward_static on the current device. */

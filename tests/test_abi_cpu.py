@@ -104,3 +104,46 @@ def test_capacities_match_reference_planner():
         cap = B.capacities(wl.parent, wl.seq_start)
         assert cap["max_forks"] == ref["n_fork"]
         assert cap["max_levels"] == max(1, ref["n_levels"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"dtype": 0}, -3),
+    ({"D": 64}, -2),
+    ({"Hq": 6, "Hkv": 4}, -2),
+    ({"Hkv": 0}, -2),
+    ({"max_levels": 0}, -2),
+    ({"max_levels": 65}, -2),
+    ({"T": -1}, -2),
+])
+def test_attention_bad_dims_are_rejected_on_the_host(kw, code):
+    from tree_forked_gated_amd import binding as B
+    base = dict(T=100, Hq=8, Hkv=2, D=128, n_seq=1, dtype=B.GDN_BF16, max_levels=4)
+    base.update(kw)
+    d = B.AttnDims(base["T"], base["Hq"], base["Hkv"], base["D"], base["n_seq"], base["dtype"], base["max_levels"])
+    n = ctypes.c_size_t(0)
+    assert B.lib.gdn_tree_attention_workspace_size(ctypes.byref(d), ctypes.byref(n)) == code
+
+
+def test_attention_argument_errors_need_no_gpu():
+    from tree_forked_gated_amd import binding as B
+    assert B.lib.gdn_tree_attention(None, None) == -1
+    d = B.attention_dims(100, 8, 2, 128, 1, 2)
+    n = B.attention_workspace_size(d)
+    assert n > 100 * (16 + 8 * 2)  # item and span tables on top of the planner's
+    a = B.AttnArgs()
+    a.dims = d
+    a.scale = 0.1
+    assert B.lib.gdn_tree_attention(ctypes.byref(a), None) == -1  # pointers missing
+    for f in ["q", "k", "v", "out", "parent_idx", "seq_start", "workspace"]:
+        setattr(a, f, ctypes.c_void_p(4096))
+    a.workspace_bytes = 16
+    assert B.lib.gdn_tree_attention(ctypes.byref(a), None) == -4  # workspace too small
+    a.workspace_bytes = n
+    a.k = ctypes.c_void_p(4100)
+    assert B.lib.gdn_tree_attention(ctypes.byref(a), None) == -6  # misaligned
+    a.k = ctypes.c_void_p(4096)
+    a.flags = 2
+    assert B.lib.gdn_tree_attention(ctypes.byref(a), None) == -6  # unknown flag
+    a.flags = 0
+    a.scale = float("nan")
+    assert B.lib.gdn_tree_attention(ctypes.byref(a), None) == -6

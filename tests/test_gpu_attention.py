@@ -1,0 +1,170 @@
+"""ForkAttention on the GPU (gdn_tree_attention) against the fp64 oracle
+(oracle/attention.py), element by element.
+
+Tolerance: relative L2 1e-2 over the outputs (bf16 inputs and outputs, fp32
+softmax state, probabilities rounded to bf16 for the value product), plus a
+per-row bound of 5e-2 of the typical row norm. Cases: sequences of 1, 63, 64,
+65, 127, 128 and 129 tokens (tile boundaries), an empty sequence, forks from
+the last and first token of a tile and from mid-tile tokens, nested forks, draft
+trees (tree chunks), grouped key/value heads; at full size the decision-round
+structure with sampled rows; bitwise request isolation; plan reuse; the level
+capacity error.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import fork_attention
+from tree_forked_gated_amd import workloads as W
+
+from gpu_helpers import record_margin, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+ROW_TOL = 5e-2
+
+
+def _values(rng, T, Hq, Hkv, D=128):
+    """bf16-exact q, k, v: standard normal, q and k L2-normalised then scaled
+    so that logits spread over a few units."""
+    q = W._normal_f32(rng, (T, Hq, D), unit_rows=True) * 4.0
+    k = W._normal_f32(rng, (T, Hkv, D), unit_rows=True) * 4.0
+    v = W._normal_f32(rng, (T, Hkv, D))
+    return W.bf16_round(q), W.bf16_round(k), W.bf16_round(v)
+
+
+def _stream(lens, forks=(), drafts=()):
+    """Chains of the given lengths plus branches (sequence, local fork token,
+    length) appended to their sequence, then draft trees of the given sizes."""
+    rng = np.random.default_rng(5)
+    parents, starts, used = [], [0], 0
+    for s, L in enumerate(lens):
+        par = list(range(-1, L - 1)) if L else []
+        for fs, ft, bl in forks:
+            if fs == s:
+                b0 = len(par)
+                par += [ft] + list(range(b0, b0 + bl - 1))
+        parents.append(np.array([p + used if p >= 0 else -1 for p in par], np.int64))
+        used += len(par)
+        starts.append(used)
+    for n in drafts:
+        lp = W.random_draft_tree(rng, n)
+        parents.append(np.where(lp < 0, -1, lp + used))
+        used += n
+        starts.append(used)
+    return np.concatenate(parents).astype(np.int32), np.array(starts, np.int32)
+
+
+def _levels(parent, seq_start):
+    from tree_forked_gated_amd import binding as B
+    return B.capacities(parent, seq_start)["max_levels"]
+
+
+def _run(parent, seq_start, q, k, v, scale, **kw):
+    from tree_forked_gated_amd import binding as B
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(torch.bfloat16)
+    out, ws = B.attention(f(q), f(k), f(v), parent, seq_start, scale=scale,
+                          max_levels=kw.pop("max_levels", _levels(parent, seq_start)), check=True, **kw)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+def _compare(name, got, ref):
+    g = np.asarray(got, np.float64)
+    e = rel_l2(g, ref)
+    err = np.sqrt(np.sum((g - ref) ** 2, axis=-1))
+    worst = float(err.max() / max(np.sqrt(np.mean(np.sum(ref ** 2, axis=-1))), 1e-30))
+    say(f"  {name}: rel-L2 {e:.3e}, worst row {worst:.3e}")
+    record_margin(f"attention/{name}", tol=1e-2, row_tol=ROW_TOL, out=e, worst_row=worst)
+    assert e <= 1e-2 and worst <= ROW_TOL, (name, e, worst)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (8, 1)])
+def test_tile_boundaries_forks_and_trees(Hq, Hkv):
+    parent, seq = _stream([1, 63, 64, 0, 65, 127, 128, 129, 300],
+                          forks=[(8, 63, 40), (8, 64, 70), (7, 127, 3), (6, 126, 65), (8, 200, 90), (8, 0, 5),
+                                 (8, 310, 20)],  # the last one forks inside the first branch (nested)
+                          drafts=[1, 17, 64])
+    T = parent.shape[0]
+    rng = np.random.default_rng(11)
+    q, k, v = _values(rng, T, Hq, Hkv)
+    say(f"attention boundaries: T={T} Hq={Hq} Hkv={Hkv}")
+    out, _ = _run(parent, seq, q, k, v, 128 ** -0.5)
+    ref = fork_attention(q, k, v, parent, seq, 128 ** -0.5)
+    _compare(f"boundaries_h{Hq}_{Hkv}", out.float().cpu().numpy(), ref)
+
+
+def test_nested_forests_and_scale():
+    wl = W.mixed_forest(seed=77, total=3000, H=1, D=16)  # structure only
+    parent, seq = wl.parent, wl.seq_start
+    T = parent.shape[0]
+    rng = np.random.default_rng(12)
+    q, k, v = _values(rng, T, 4, 2)
+    say(f"attention nested forests: T={T}, levels {_levels(parent, seq)}")
+    for scale in (128 ** -0.5, 0.25):
+        out, _ = _run(parent, seq, q, k, v, scale)
+        ref = fork_attention(q, k, v, parent, seq, scale)
+        _compare(f"forests_scale{scale:.3f}", out.float().cpu().numpy(), ref)
+
+
+def test_decision_round_full_size_sampled_rows():
+    """The decision-round structure at full size (8 requests x (8192-token
+    trunk + 16 x 32-token questions), 16 query heads over 2 key/value heads);
+    the oracle computes 96 sampled rows one by one."""
+    wl = W.decision_round(H=1, D=16)  # structure only
+    parent, seq = wl.parent, wl.seq_start
+    T = parent.shape[0]
+    rng = np.random.default_rng(13)
+    q, k, v = _values(rng, T, 16, 2)
+    say(f"attention decision round: T={T}")
+    out, _ = _run(parent, seq, q, k, v, 128 ** -0.5)
+    rows = np.unique(np.concatenate([wl.out_rows[::4], rng.integers(0, T, 48), [0, 8191, 8192, T - 1]]))
+    ref = fork_attention(q, k, v, parent, seq, 128 ** -0.5, rows=rows)
+    _compare("decision_round_sampled", out.float().cpu().numpy()[rows], ref)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16)
+
+
+def test_request_isolation_bitwise_and_plan_reuse():
+    from tree_forked_gated_amd import binding as B
+    pa, sa = _stream([200], forks=[(0, 150, 70), (0, 199, 9)])
+    pb, sb = _stream([90, 40], forks=[(0, 30, 64)], drafts=[20])
+    na, nb = pa.shape[0], pb.shape[0]
+    rng = np.random.default_rng(14)
+    qa, ka, va = _values(rng, na, 4, 2)
+    qb, kb, vb = _values(rng, nb, 4, 2)
+    # A after B in one stream, and A alone
+    parent = np.concatenate([pb, np.where(pa < 0, -1, pa + nb)]).astype(np.int32)
+    seq = np.concatenate([sb, sa[1:] + nb]).astype(np.int32)
+    cat = lambda x, y: np.concatenate([y, x])
+    both, ws = _run(parent, seq, cat(qa, qb), cat(ka, kb), cat(va, vb), 0.1)
+    alone, _ = _run(pa, sa, qa, ka, va, 0.1)
+    say(f"attention isolation: A alone T={na}, inside a stream of T={na + nb}")
+    assert torch.equal(_bits(both[nb:]), _bits(alone))
+    # the planned workspace serves a second call with the same structure bit for bit
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(torch.bfloat16)
+    again, _ = B.attention(f(cat(qa, qb)), f(cat(ka, kb)), f(cat(va, vb)), parent, seq, scale=0.1,
+                           max_levels=_levels(parent, seq), workspace=ws, planned=True, check=True)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(again), _bits(both))
+    # a workspace planned for other sizes is refused on the device
+    with pytest.raises(B.GdnDeviceError) as ei:
+        B.attention(f(qa), f(ka), f(va), pa, sa, scale=0.1, max_levels=_levels(parent, seq),
+                    workspace=ws, planned=True, check=True)
+    assert ei.value.code == 8
+
+
+def test_level_capacity_is_reported():
+    from tree_forked_gated_amd import binding as B
+    parent, seq = _stream([200], forks=[(0, 100, 80), (0, 250, 10)])  # the second branch nests in the first
+    assert _levels(parent, seq) == 3
+    rng = np.random.default_rng(15)
+    q, k, v = _values(rng, parent.shape[0], 2, 2)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(torch.bfloat16)
+    out = torch.full((parent.shape[0], 2, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.GdnDeviceError) as ei:
+        B.attention(f(q), f(k), f(v), parent, seq, max_levels=2, out=out, check=True)
+    assert ei.value.code == 5
+    assert bool((out == 3.0).all())  # nothing computed

@@ -49,6 +49,20 @@ class CommitArgs(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class AttnDims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("n_seq", ctypes.c_int32), ("dtype", ctypes.c_int32), ("max_levels", ctypes.c_int32)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("dims", AttnDims), ("scale", ctypes.c_float), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("parent_idx", ctypes.c_void_p), ("seq_start", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("flags", ctypes.c_uint32)]
+
+
+ATTN_PLANNED = 1  # gdn_tree.h GDN_ATTN_PLANNED
+
 _LAYOUT_FIELDS = ["err", "n_seg", "n_fork", "tok_seq", "depth", "fork_slot", "seg_start", "seg_len", "seg_seq",
                   "seg_mode", "seg_entry", "seg_slot", "seg_level", "level_count", "level_ptr", "level_items",
                   "tree_mask", "fork_states", "total"]
@@ -60,7 +74,8 @@ class Layout(ctypes.Structure):
 
 EXPORTS = ["gdn_tree_workspace_size", "gdn_tree_plan_layout", "gdn_tree_commit_workspace_size", "gdn_tree_plan",
            "gdn_tree_forward", "gdn_tree_forward_static", "gdn_tree_commit", "gdn_tree_check_error",
-           "gdn_tree_strerror", "gdn_tree_last_error", "gdn_tree_version"]
+           "gdn_tree_strerror", "gdn_tree_last_error", "gdn_tree_version", "gdn_tree_attention_workspace_size",
+           "gdn_tree_attention"]
 STATIC_WORKSPACE_BYTES = 64 << 20  # gdn_tree.h GDN_TREE_STATIC_WORKSPACE_BYTES
 
 
@@ -75,7 +90,8 @@ def _load():
     lib.gdn_tree_last_error.restype = ctypes.c_char_p
     lib.gdn_tree_commit_workspace_size.restype = ctypes.c_size_t
     for name in ["gdn_tree_workspace_size", "gdn_tree_plan_layout", "gdn_tree_plan", "gdn_tree_forward",
-                 "gdn_tree_forward_static", "gdn_tree_commit", "gdn_tree_check_error", "gdn_tree_version"]:
+                 "gdn_tree_forward_static", "gdn_tree_commit", "gdn_tree_check_error", "gdn_tree_version",
+                 "gdn_tree_attention_workspace_size", "gdn_tree_attention"]:
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -345,6 +361,49 @@ def plan(parent_idx, seq_start, *, T=None, H=1, Dk=16, Dv=16, dtype_code=GDN_F32
     for f in ["seg_start", "seg_len", "seg_seq", "seg_mode", "seg_entry", "seg_slot", "seg_level", "level_items"]:
         out[f] = i32(f, T)[:n_seg]
     return out
+
+
+# ----------------------------------------------------------------- attention
+
+def attention_dims(T, Hq, Hkv, D, n_seq, max_levels) -> AttnDims:
+    return AttnDims(int(T), int(Hq), int(Hkv), int(D), int(n_seq), GDN_BF16, int(max_levels))
+
+
+def attention_workspace_size(dims: AttnDims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.gdn_tree_attention_workspace_size(ctypes.byref(dims), ctypes.byref(n)),
+           "gdn_tree_attention_workspace_size")
+    return int(n.value)
+
+
+def attention(q, k, v, parent_idx, seq_start, *, max_levels, scale=None, workspace=None, out=None, planned=False,
+              stream=None, check=False):
+    """gdn_tree_attention (ForkAttention) on device tensors: q [T,Hq,D], k and
+    v [T,Hkv,D] bf16; returns (out [T,Hq,D], workspace). max_levels is the
+    fork-nesting capacity (as for forward); scale defaults to 1/sqrt(D)."""
+    device = q.device
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    parent_idx = _i32(parent_idx, device)
+    seq_start = _i32(seq_start, device)
+    dims = attention_dims(T, Hq, Hkv, D, seq_start.numel() - 1, max_levels)
+    if workspace is None:
+        workspace = torch.empty(attention_workspace_size(dims), dtype=torch.uint8, device=device)
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=q.dtype, device=device)
+    a = AttnArgs()
+    a.dims = dims
+    a.scale = float(D ** -0.5 if scale is None else scale)
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.parent_idx, a.seq_start = _ptr(parent_idx), _ptr(seq_start)
+    a.out = _ptr(out)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = int(workspace.numel())
+    a.flags = ATTN_PLANNED if planned else 0
+    _check(lib.gdn_tree_attention(ctypes.byref(a), _stream(stream)), "gdn_tree_attention")
+    if check:
+        raise_device_error(workspace, stream)
+    return out, workspace
 
 
 # -------------------------------------------------------------------- commit

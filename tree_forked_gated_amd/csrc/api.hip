@@ -319,6 +319,50 @@ int gdn_tree_commit(const gdn_tree_commit_args* a, void* stream) {
   return GDN_OK;
 }
 
+static int check_attn_dims(const gdn_attn_dims* d) {
+  if (!d) return fail(GDN_ERR_NULL, "dims is NULL");
+  if (d->dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "gdn_tree_attention takes bf16 q, k and v");
+  if (d->T < 0 || d->T > 0x7fffffffLL) return fail(GDN_ERR_DIMS, "T must be in [0, 2^31)");
+  if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv) return fail(GDN_ERR_DIMS, "Hq must be a positive multiple of Hkv");
+  if (d->D != 128) return fail(GDN_ERR_DIMS, "D must be 128");
+  if ((long long)d->Hq * d->D >= (1ll << 24)) return fail(GDN_ERR_DIMS, "Hq * D must stay below 2^24");
+  if (d->n_seq < 0) return fail(GDN_ERR_DIMS, "n_seq must be >= 0");
+  if (d->max_levels < 1 || d->max_levels > attn_max_spans())
+    return fail(GDN_ERR_DIMS, "max_levels must be in [1, 64] for gdn_tree_attention");
+  return GDN_OK;
+}
+
+int gdn_tree_attention_workspace_size(const gdn_attn_dims* dims, size_t* bytes) {
+  int rc = check_attn_dims(dims);
+  if (rc) return rc;
+  if (!bytes) return fail(GDN_ERR_NULL, "bytes is NULL");
+  AttnLayout A;
+  if (!attn_layout(*dims, &A)) return fail(GDN_ERR_DIMS, "bad sizes");
+  *bytes = A.total;
+  return GDN_OK;
+}
+
+int gdn_tree_attention(const gdn_attn_args* a, void* stream) {
+  if (!a) return fail(GDN_ERR_NULL, "args is NULL");
+  int rc = check_attn_dims(&a->dims);
+  if (rc) return rc;
+  const gdn_attn_dims& d = a->dims;
+  if (!a->seq_start || !a->workspace || (d.T > 0 && (!a->parent_idx || !a->q || !a->k || !a->v || !a->out)))
+    return fail(GDN_ERR_NULL, "seq_start, workspace and (T > 0) parent_idx, q, k, v and out are required");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out))
+    return fail(GDN_ERR_ARGS, "q, k, v and out must be 16-byte aligned");
+  if (((uintptr_t)a->workspace & 255u) != 0) return fail(GDN_ERR_ARGS, "workspace must be 256-byte aligned");
+  if (a->flags & ~GDN_ATTN_PLANNED) return fail(GDN_ERR_ARGS, "unknown flags");
+  if (!(a->scale == a->scale) || a->scale > 3.0e38f || a->scale < -3.0e38f)
+    return fail(GDN_ERR_ARGS, "scale must be finite");
+  AttnLayout A;
+  if (!attn_layout(d, &A)) return fail(GDN_ERR_DIMS, "bad sizes");
+  if (a->workspace_bytes < A.total) return fail(GDN_ERR_WORKSPACE, "workspace smaller than gdn_tree_attention_workspace_size");
+  hipError_t e = launch_attention(*a, A, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "gdn_tree_attention");
+  return GDN_OK;
+}
+
 int gdn_tree_check_error(const void* workspace, void* stream, int32_t* code, int64_t* index) {
   if (!code || !index) return fail(GDN_ERR_NULL, "code and index are required");
   if (!workspace) {  // the static workspace of gdn_tree_forward_static on the current device

@@ -1,0 +1,463 @@
+// ForkAttention for the full-attention layers of a tree-structured flat stream
+// (Flide, "Accelerating Decision Inference with Exact State Forking", section
+// 3.2.1 "Full-Attention Layers" and section 3.3.1 "GPU-Resident Metadata").
+//
+// Token t attends to its ancestors-or-self in its own sequence (the visibility
+// rule under which every question computes its standalone prompt, section
+// 3.2.3). On the segment table of the recurrence's planner (a segment is a
+// maximal run of tokens each the child of the one before; a sequence of at most
+// 64 tokens is one tree chunk), the keys visible to the queries of one 64-token
+// chunk of a segment are key spans:
+//
+//   * the segment's own prefix [segment start, last query of the chunk], whose
+//     tiles before the chunk are fully visible and whose last tile (the chunk
+//     itself) is causal, and
+//   * for every ancestor segment on the root path, its prefix up to the fork
+//     token the path leaves it at, fully visible except for a span's last tile
+//     when the fork token is not a tile's last key.
+//
+// A tree chunk has one tile, masked by its ancestor bits. Other requests'
+// tokens are never in a span. The span lists are built on the GPU (one
+// planning workgroup, after the recurrence's metadata kernels), so launch
+// shapes depend only on the sizes.
+//
+// The attention kernel is a persistent grid of 4-wave workgroups that claim
+// (chunk, query head) items. Each wave owns 16 queries and walks the item's key
+// tiles of 64 keys with an online softmax: S^T = K Q^T and O^T += V^T P^T on
+// 16x16x32 bf16 matrix cores, fp32 softmax state. K and V tiles are copied
+// straight from HBM into LDS one tile ahead (double-buffered). Fully visible
+// tiles take no mask.
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int D = 128;        // head dimension
+constexpr int kT = 64;        // keys per tile, queries per chunk
+constexpr int kThr = 256;     // four waves
+constexpr int kTileB = kT * D * 2;  // bytes of one K or V tile (bf16)
+constexpr int kMaxSpans = 64;  // span capacity per item (fork nesting levels)
+constexpr int oK = 0;                   // [2] K tiles
+constexpr int oV = 2 * kTileB;          // [2] V tiles
+constexpr int oSp = 4 * kTileB;         // the item's spans (int2)
+constexpr int kLds = oSp + 8 * kMaxSpans;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* out;
+  const unsigned long long* err;
+  const unsigned long long* tree_mask;
+  const int4* item_info;  // {first query, queries, mode | sequence << 1, spans}
+  const int2* spans;      // [item][max_levels] inclusive key spans; span 0 is the item's own segment
+  const int* n_items;
+  int* claim;
+  int Hq, Hkv, max_levels;
+  float c;  // scale * log2(e)
+};
+
+__device__ __forceinline__ void dma16(const void* sbase, unsigned voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
+               : "memory");
+}
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ uint32_t lds_addr_of(const unsigned char* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((const lds_void*)p));
+}
+__device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// 16-byte piece p of tile row r sits at slot p ^ swz(r) (spreads the rows over the LDS banks)
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ i16x4 tr_read(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+__device__ __forceinline__ bf16x8 cat8(i16x4 lo, i16x4 hi) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ bf16x8 cat8b(bf16x4 lo, bf16x4 hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
+__device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
+  bf16x4 r;
+  r[0] = (__bf16)x[0];
+  r[1] = (__bf16)x[1];
+  r[2] = (__bf16)x[2];
+  r[3] = (__bf16)x[3];
+  return r;
+}
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+
+// Rows [row0, row0 + n) of one key/value head (row stride rs bytes) into a
+// tile: wave w copies the 4-row blocks 4 w .. 4 w + 3; lane (g4, l16) copies
+// row 4 blk + g4, piece l16 ^ swz(row) into slot l16. Rows at or past n are
+// zero-filled and never read from memory.
+__device__ __forceinline__ void issue_tile(const __bf16* head0, int row0, int n, unsigned rs, unsigned char* tile,
+                                           int w, int lane) {
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(head0) + (size_t)row0 * rs + (size_t)(16 * w) * rs;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int blk = 4 * w + b;
+    const unsigned vo = g4 * rs + (unsigned)((l16 ^ ((g4 << 2) | (blk & 3))) << 4);
+    if (4 * blk + g4 < n) dma16(src, vo, lds_addr_of(tile + blk * 1024));
+    else *reinterpret_cast<uint4*>(tile + blk * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
+    src += (size_t)4 * rs;
+  }
+}
+
+// One key tile of an item: its first key, valid keys, and mask kind.
+struct Tile {
+  int valid, k0, n, kind;  // kind 0: no mask beyond n; 1: causal (the item's own chunk); 2: tree ancestor bits
+  int sp;                  // span index
+};
+
+// The tile after (sp, k0) in the item's span list (spans in LDS).
+__device__ __forceinline__ Tile next_tile(const int2* sps, int nsp, int sp, int k0, int q0, int tree) {
+  Tile t = {0, 0, 0, 0, 0};
+  while (sp < nsp) {
+    const int2 s = sps[sp];
+    if (k0 < 0) k0 = s.x;
+    if (k0 <= s.y) {
+      t.valid = 1;
+      t.sp = sp;
+      t.k0 = k0;
+      t.n = min(kT, s.y - k0 + 1);
+      t.kind = (sp == 0 && k0 == q0) ? (tree ? 2 : 1) : 0;
+      return t;
+    }
+    ++sp;
+    k0 = -1;
+  }
+  return t;
+}
+
+__global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int s_claim;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = rfl(tid >> 6);
+  const int g4 = lane >> 4, l16 = lane & 15;
+  if (*a.err != kNoError) return;  // structural error in the tree: nothing is computed
+  const int n_items = *a.n_items;
+  const long long total = (long long)n_items * a.Hq;
+  const int G = a.Hq / a.Hkv;
+  const unsigned rs_q = (unsigned)a.Hq * (D * 2), rs_kv = (unsigned)a.Hkv * (D * 2);
+  int2* sps = reinterpret_cast<int2*>(smem + oSp);
+  // A-operand rows of the K fragments (row l16 of a 16-key block, d 32 ks + 8 g4 .. + 7)
+  int oF[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) oF[ks] = l16 * 256 + (((4 * ks + g4) ^ swz(l16)) << 4);
+  // transposed reads of V: lane i of a 16-lane group receives d column 32 m + 8 (i / 4) + 4 bb + i % 4 of
+  // keys 4 g4 .. 4 g4 + 3 (dt = 2 m + bb); the accumulator element r of O^T block dt is then
+  // d = 32 m + 8 g4 + 4 bb + r for query l16
+  int oT[8];
+  {
+    const int r0 = 4 * g4 + (l16 >> 2), p = l16 & 3;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oT[dt] = r0 * 256 + ((((4 * (dt >> 1) + p) ^ swz(r0))) << 4) + ((dt & 1) << 3);
+  }
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  for (;;) {
+    if (tid == 0) s_claim = atomicAdd(a.claim, 1);
+    __syncthreads();
+    const long long idx = s_claim;
+    if (idx >= total) break;
+    const int item = (int)(idx / a.Hq), h = (int)(idx % a.Hq);
+    const int hk = h / G;
+    const int4 inf = a.item_info[item];
+    const int q0 = rfl(inf.x), nq = rfl(inf.y), tree = rfl(inf.z & 1), sq = rfl(inf.z >> 1);
+    const int nsp = rfl(min(inf.w, kMaxSpans));
+    if (tid < nsp) sps[tid] = a.spans[(size_t)item * a.max_levels + tid];
+    // this wave's 16 queries as MFMA fragments (zero past the chunk's queries)
+    const int qi = 16 * w + l16;  // query within the chunk
+    bf16x8 Qf[4];
+    unsigned long long tmask = 0;
+    {
+      const bool ok = qi < nq;
+      const __bf16* qrow = a.q + ((size_t)(q0 + (ok ? qi : 0)) * a.Hq + h) * D;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g4);
+        if (!ok) x = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+        Qf[ks] = x;
+      }
+      if (tree && ok) tmask = a.tree_mask[(size_t)sq * kT + qi];
+    }
+    const __bf16* k0p = a.k + (size_t)hk * D;
+    const __bf16* v0p = a.v + (size_t)hk * D;
+    __syncthreads();  // spans in LDS
+    Tile cur = next_tile(sps, nsp, 0, -1, q0, tree);
+    if (cur.valid) {
+      issue_tile(k0p, cur.k0, cur.n, rs_kv, smem + oK, w, lane);
+      issue_tile(v0p, cur.k0, cur.n, rs_kv, smem + oV, w, lane);
+    }
+    wait_vm();
+    lds_barrier();
+    f32x4 O[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) O[dt] = zero;
+    float m = -INFINITY, l = 0.f;
+    const bool active = 16 * w < nq;
+    for (int it = 0; cur.valid; ++it) {
+      const Tile nxt = next_tile(sps, nsp, cur.sp, cur.k0 + kT, q0, tree);
+      const int b = it & 1;
+      if (nxt.valid) {
+        issue_tile(k0p, nxt.k0, nxt.n, rs_kv, smem + oK + (b ^ 1) * kTileB, w, lane);
+        issue_tile(v0p, nxt.k0, nxt.n, rs_kv, smem + oV + (b ^ 1) * kTileB, w, lane);
+      }
+      if (active) {
+        const unsigned char* kt = smem + oK + b * kTileB;
+        const unsigned char* vt = smem + oV + b * kTileB;
+        // S^T = K Q^T: lane (query l16, g4) holds keys 16 kb + 4 g4 + r
+        f32x4 S[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          S[kb] = zero;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            S[kb] = mma32(*reinterpret_cast<const bf16x8*>(kt + kb * 4096 + oF[ks]), Qf[ks], S[kb]);
+        }
+        float x[4][4];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kk = 16 * kb + 4 * g4 + r;
+            bool ok = kk < cur.n;
+            if (cur.kind == 1) ok = ok && kk <= qi;
+            else if (cur.kind == 2) ok = ok && ((tmask >> kk) & 1ull);
+            x[kb][r] = ok ? S[kb][r] * a.c : -INFINITY;
+            mt = fmaxf(mt, x[kb][r]);
+          }
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);
+        f32x4 P[4];
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            P[kb][r] = __builtin_amdgcn_exp2f(x[kb][r] - mref);
+            ls += P[kb][r];
+          }
+        l = l * alpha + ls;
+        m = mn;
+        const bf16x8 w01 = cat8b(to_bf4(P[0]), to_bf4(P[1]));
+        const bf16x8 w23 = cat8b(to_bf4(P[2]), to_bf4(P[3]));
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const unsigned char* vp = vt + oT[dt];
+          f32x4 o = O[dt];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] *= alpha;
+          o = mma32(cat8(tr_read(vp), tr_read(vp + 4096)), w01, o);
+          O[dt] = mma32(cat8(tr_read(vp + 8192), tr_read(vp + 12288)), w23, o);
+        }
+      }
+      wait_vm();  // the next tile has landed
+      lds_barrier();
+      cur = nxt;
+    }
+    if (active) {
+      float lt = l + __shfl_xor(l, 16);
+      lt += __shfl_xor(lt, 32);
+      const float inv = 1.f / lt;
+      if (qi < nq) {
+        __bf16* orow = a.out + ((size_t)(q0 + qi) * a.Hq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          f32x4 o = O[dt];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] *= inv;
+          *reinterpret_cast<bf16x4*>(orow + 32 * (dt >> 1) + 8 * g4 + 4 * (dt & 1)) = to_bf4(o);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- item tables
+
+struct ItemTables {
+  int4* item_info;
+  int2* spans;
+  int* item_off;
+  int* n_items;
+  int* claim;
+};
+
+// Exclusive scan over a 1024-thread block; *total gets the sum.
+__device__ inline int block_scan(int v, int* sh, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wv] = x;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 16; ++i) {
+      const int t = sh[i];
+      sh[i] = run;
+      run += t;
+    }
+    sh[16] = run;
+  }
+  __syncthreads();
+  const int ex = sh[wv] + x - v;
+  *total = sh[16];
+  __syncthreads();
+  return ex;
+}
+
+__device__ inline int seg_containing(const int* seg_start, int n_seg, int t) {
+  int lo = 0, hi = n_seg;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (seg_start[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// One workgroup: chunk items of every segment (in stream order) and each
+// item's key spans: its own segment's prefix, then the ancestor segments' prefixes.
+__global__ void __launch_bounds__(1024) k_attn_items(Meta m, ItemTables t, int max_levels) {
+  __shared__ int sh[17];
+  const int tid = threadIdx.x;
+  const int n_seg = (*m.err != kNoError) ? 0 : *m.n_seg;
+  int run = 0;
+  for (int base = 0; base < n_seg; base += 1024) {
+    const int s = base + tid;
+    const int nch = s < n_seg ? (m.seg_mode[s] ? 1 : (m.seg_len[s] + kT - 1) / kT) : 0;
+    int tot;
+    const int ex = block_scan(nch, sh, &tot);
+    if (s < n_seg) t.item_off[s] = run + ex;
+    run += tot;
+  }
+  if (tid == 0) {
+    *t.n_items = run;
+    *t.claim = 0;
+  }
+  __syncthreads();
+  for (int s = tid; s < n_seg; s += 1024) {
+    const int st = m.seg_start[s], len = m.seg_len[s], mode = m.seg_mode[s], sq = m.seg_seq[s];
+    const int nch = mode ? 1 : (len + kT - 1) / kT;
+    const int off = t.item_off[s];
+    int nsp = 1;
+    int e = m.seg_entry[s];
+    while (e >= 0 && nsp < max_levels) {  // the planner bounds the nesting below max_levels
+      const int p = seg_containing(m.seg_start, n_seg, e);
+      const int2 span = make_int2(m.seg_start[p], e);
+      for (int c = 0; c < nch; ++c) t.spans[(size_t)(off + c) * max_levels + nsp] = span;
+      ++nsp;
+      e = m.seg_entry[p];
+    }
+    for (int c = 0; c < nch; ++c) {
+      const int q0 = st + kT * c, nq = mode ? len : min(kT, len - kT * c);
+      t.spans[(size_t)(off + c) * max_levels] = make_int2(st, q0 + nq - 1);
+      t.item_info[off + c] = make_int4(q0, nq, mode | (sq << 1), nsp);
+    }
+  }
+}
+
+__global__ void k_attn_replan(Meta m, int* claim, unsigned long long tag) {
+  if (threadIdx.x == 0) {
+    *claim = 0;
+    if (*m.plan_tag != tag) raise_error(m.err, GDN_DEV_NOT_PLANNED, 0);
+  }
+}
+
+}  // namespace
+
+bool attn_layout(const gdn_attn_dims& d, AttnLayout* A) {
+  gdn_tree_dims pd = {};
+  pd.T = d.T;
+  pd.H = 1;
+  pd.Dk = 0;  // no fork-state slots: the attention reads the segment tables only
+  pd.Dv = 0;
+  pd.n_seq = d.n_seq;
+  pd.dtype = d.dtype;
+  pd.max_forks = (int)(d.T > 0x7fffffff ? 0x7fffffff : d.T);
+  pd.max_levels = d.max_levels;
+  if (!compute_layout(pd, &A->plan)) return false;
+  A->pd = pd;
+  const size_t T = (size_t)(d.T > 0 ? d.T : 0);
+  size_t off = A->plan.pub.total;
+  auto take = [&](size_t bytes) { size_t o = off; off = (off + bytes + 255) & ~(size_t)255; return o; };
+  A->item_info = take(16 * T);
+  A->spans = take(8 * T * (size_t)d.max_levels);
+  A->item_off = take(4 * T);
+  A->n_items = take(4);
+  A->claim = take(4);
+  A->total = off;
+  return true;
+}
+
+hipError_t launch_attention(const gdn_attn_args& aa, const AttnLayout& A, hipStream_t s) {
+  char* ws = (char*)aa.workspace;
+  Meta m = meta_from(ws, A.plan);
+  ItemTables t;
+  t.item_info = (int4*)(ws + A.item_info);
+  t.spans = (int2*)(ws + A.spans);
+  t.item_off = (int*)(ws + A.item_off);
+  t.n_items = (int*)(ws + A.n_items);
+  t.claim = (int*)(ws + A.claim);
+  gdn_tree_fwd_args pa = {};
+  pa.dims = A.pd;
+  pa.parent_idx = aa.parent_idx;
+  pa.seq_start = aa.seq_start;
+  pa.workspace = aa.workspace;
+  pa.workspace_bytes = aa.workspace_bytes;
+  const unsigned long long tag = plan_fingerprint(pa);
+  hipError_t e;
+  if (aa.flags & GDN_ATTN_PLANNED) {
+    hipLaunchKernelGGL(k_attn_replan, dim3(1), dim3(64), 0, s, m, t.claim, tag);
+  } else {
+    e = launch_plan(pa, m, A.plan, tag, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_attn_items, dim3(1), dim3(1024), 0, s, m, t, aa.dims.max_levels);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (aa.dims.T == 0 || aa.dims.n_seq == 0) return hipSuccess;
+  AttnArgs x;
+  x.q = reinterpret_cast<const __bf16*>(aa.q);
+  x.k = reinterpret_cast<const __bf16*>(aa.k);
+  x.v = reinterpret_cast<const __bf16*>(aa.v);
+  x.out = reinterpret_cast<__bf16*>(aa.out);
+  x.err = m.err;
+  x.tree_mask = m.tree_mask;
+  x.item_info = t.item_info;
+  x.spans = t.spans;
+  x.n_items = t.n_items;
+  x.claim = t.claim;
+  x.Hq = aa.dims.Hq;
+  x.Hkv = aa.dims.Hkv;
+  x.max_levels = aa.dims.max_levels;
+  x.c = aa.scale * kLog2e;
+  int cus = 0, occ = 1;
+  e = ensure_dynamic_lds(reinterpret_cast<const void*>(k_fork_attn), kLds, kThr, &occ);
+  if (e != hipSuccess) return e;
+  e = current_device_cus(&cus);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_fork_attn, dim3(cus * occ), dim3(kThr), kLds, s, x);
+  return hipGetLastError();
+}
+
+int attn_max_spans() { return kMaxSpans; }
+
+}  // namespace gdn

@@ -95,4 +95,15 @@ bool walk_pipe_supported(int dtype, int dk, int bv);
 hipError_t launch_walk_pipe(const gdn_tree_fwd_args& a, const Meta& m, int bv, hipStream_t s);
 int walk_lds_bytes(int dtype, int dk, int bv);
 
+// ForkAttention (attention.hip): the workspace is the planner's layout for the
+// stream (without fork-state slots), then the attention's item and span tables.
+struct AttnLayout {
+  LayoutFull plan;
+  gdn_tree_dims pd;  // the sizes the planner runs with
+  size_t item_info, spans, item_off, n_items, claim, total;
+};
+bool attn_layout(const gdn_attn_dims& d, AttnLayout* A);
+hipError_t launch_attention(const gdn_attn_args& a, const AttnLayout& A, hipStream_t s);
+int attn_max_spans();
+
 }  // namespace gdn
