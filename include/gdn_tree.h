@@ -102,6 +102,8 @@ typedef enum gdn_dev_error {
   GDN_DEV_ROWS = 6,           /* out_rows / state_rows entry outside [0, T) or repeated; index = position */
   GDN_DEV_PATH = 7,           /* commit path is not a root-to-node parent chain; index = path number */
   GDN_DEV_NOT_PLANNED = 8,    /* GDN_FWD_PLANNED on a workspace without a matching plan; index = 0 */
+  GDN_DEV_CHAIN = 9,          /* gdn_chain_step: an accepted count outside [0, N] or a history length outside
+                                 [0, hist_cap]; index = the first such sequence (it is skipped) */
 } gdn_dev_error;
 
 /*
@@ -345,6 +347,75 @@ int gdn_tree_attention_workspace_size(const gdn_attn_dims* dims, size_t* bytes);
 /* ForkAttention over the stream: metadata (unless GDN_ATTN_PLANNED), then the
  * attention kernel. Enqueue only. */
 int gdn_tree_attention(const gdn_attn_args* a, void* stream);
+
+/*
+ * One speculative round of chain drafts in one kernel (TreeWY, "Speculative
+ * Verification for Gated DeltaNet Hybrids", section 4 "Implementation": a chain
+ * verifies and commits in one fused, graph-capturable kernel), with the
+ * committed state written only at a flush (the deferred write of ReplaySSM, the
+ * prior point TreeWY's section 1 and appendix D compare against).
+ *
+ * Per sequence s the call
+ *  1. rebuilds the committed state S from the checkpoint, the history of
+ *     accepted tokens since it, and the first accepted[s] tokens of the previous
+ *     draft (TreeWY Eq. 3 over that path);
+ *  2. flushes (writes S to ckpt and empties the history) when GDN_CHAIN_FLUSH is
+ *     set or the history would exceed hist_cap, and otherwise appends those
+ *     accepted tokens' pseudo-values, keys and log gates to the history;
+ *     writes S to state_out when given;
+ *  3. verifies this round's chain draft of N tokens from S (TreeWY Eq. 1 with
+ *     the key rewrite, token by token in fp32): outputs and pseudo-values.
+ * The next call passes this call's k, log_gate and pseudo_v as prev_k, prev_g
+ * and prev_pv, the sampler's accepted counts, and hist_len_out as hist_len_in
+ * (callers alternate two draft buffers and two history-length buffers). The
+ * first round passes accepted = 0, hist_len_in = 0 and ckpt = the initial state.
+ *
+ * Layouts (row-major, token-major inside a sequence): ckpt, state_out [n_seq, H,
+ * Dv, Dk] fp32; hist_pv [n_seq, hist_cap, H, Dv] fp32; hist_k [n_seq, hist_cap,
+ * H, Dk] dtype; hist_g [n_seq, hist_cap, H] fp32; prev_pv, pseudo_v, out
+ * [n_seq, N, H, Dv] (pv fp32, out dtype); prev_k, q, k [n_seq, N, H, Dk];
+ * v [n_seq, N, H, Dv]; prev_g, log_gate, beta [n_seq, N, H]; accepted,
+ * hist_len_in, hist_len_out [n_seq] int32. Sizes: N in [1, 32], Dk in {32, 64,
+ * 128}, Dv a multiple of 16 up to 128, hist_cap >= 0 (0: the state is written
+ * every round). workspace: at least gdn_tree_commit_workspace_size() bytes; its
+ * error word (GDN_DEV_CHAIN) is read with gdn_tree_check_error.
+ */
+#define GDN_CHAIN_FLUSH 1u
+
+typedef struct gdn_chain_dims {
+  int32_t n_seq;
+  int32_t N;
+  int32_t H, Dk, Dv;
+  int32_t dtype;
+  int32_t hist_cap;
+} gdn_chain_dims;
+
+typedef struct gdn_chain_args {
+  gdn_chain_dims dims;
+  float* ckpt;
+  float* hist_pv;
+  void* hist_k;
+  float* hist_g;
+  const int32_t* hist_len_in;
+  int32_t* hist_len_out;
+  const float* prev_pv;
+  const void* prev_k;
+  const void* prev_g;
+  const int32_t* accepted;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* log_gate;
+  const void* beta;
+  void* out;
+  float* pseudo_v;
+  float* state_out;
+  void* workspace;
+  size_t workspace_bytes;
+  uint32_t flags;
+} gdn_chain_args;
+
+int gdn_chain_step(const gdn_chain_args* a, void* stream);
 
 /* Synchronises `stream`, then reads the workspace's error word. *code gets a
  * gdn_dev_error, *index its index (0 when there is no error). workspace NULL:

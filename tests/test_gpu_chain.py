@@ -1,0 +1,85 @@
+"""Fused chain verify + commit with the deferred state write (gdn_chain_step)
+against the speculative chain-round oracle (oracle/chain.py).
+
+Eight rounds of chain drafts per sequence, with seeded accepted counts
+(including rounds that accept nothing and rounds that accept the whole draft).
+Every round's outputs and pseudo-values, and the committed state it starts from
+(state_out), are compared with the oracle: with the state written every round
+(history capacity 0), with a short history that flushes every few rounds, and
+with a history long enough that nothing flushes until a forced flush. After
+the forced flush the checkpoint itself must hold the committed state. A bad
+accepted count is reported on the device and its sequence skipped.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.chain import chain_rounds
+from tree_forked_gated_amd import workloads as W
+
+from gpu_helpers import record_margin, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _draft(rng, n_seq, N, H, D, dtype):
+    q, k, v, beta, g = W._values(rng, n_seq * N, H, D, D, dtype)
+    sh = lambda a: a.reshape((n_seq, N) + a.shape[1:])
+    return {"q": sh(q), "k": sh(k), "v": sh(v), "beta": sh(beta), "log_gate": sh(g)}
+
+
+@pytest.mark.parametrize("dtype,D,cap", [("bf16", 128, 0), ("bf16", 128, 6), ("bf16", 128, 64), ("f32", 32, 5),
+                                         ("f32", 64, 0)])
+def test_chain_rounds_against_oracle(dtype, D, cap):
+    from tree_forked_gated_amd import binding as B
+    rng = np.random.default_rng(100 + cap + D)
+    n_seq, N, H, R = 5, 4, 3, 8
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    S0 = W._init(rng, n_seq, H, D, D, True)
+    rounds = [_draft(rng, n_seq, N, H, D, dtype) for _ in range(R)]
+    acc = [rng.integers(0, N + 1, n_seq) for _ in range(R)]
+    acc[2][:] = 0
+    acc[3][:] = N
+    # accepted[r] is what the sampler keeps of draft r; round r + 1 commits it
+    ref, S_end = chain_rounds(S0, rounds, acc)
+    cr = B.ChainRounds(torch.from_numpy(S0).cuda(), N, cap, tdt, keep_state=True)
+    tol = 1e-2 if dtype == "bf16" else 1e-4
+    say(f"chain rounds {dtype} D={D} hist_cap={cap}: {n_seq} sequences x {R} rounds of {N} draft tokens")
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(tdt).contiguous()
+    worst = {"out": 0.0, "pseudo_v": 0.0, "state": 0.0}
+    for r in range(R + 1):
+        prev_acc = np.zeros(n_seq, np.int32) if r == 0 else acc[r - 1].astype(np.int32)
+        last = r == R
+        draft = {kk: f(x) for kk, x in rounds[min(r, R - 1)].items()}
+        out, pv = cr.step(draft, torch.from_numpy(prev_acc).cuda(), flush=last, check=True)
+        torch.cuda.synchronize()
+        want_state = S_end if last else ref[r]["start_state"]
+        e = {"state": rel_l2(cr.state.cpu().numpy(), want_state)}
+        if not last:
+            e["out"] = rel_l2(out.float().cpu().numpy(), ref[r]["out"])
+            e["pseudo_v"] = rel_l2(pv.cpu().numpy(), ref[r]["pseudo_v"])
+        for kk, x in e.items():
+            worst[kk] = max(worst[kk], x)
+            assert x <= tol, (r, kk, x)
+    # the forced flush leaves the committed state in the checkpoint and an empty history
+    ck = rel_l2(cr.ckpt.cpu().numpy(), S_end)
+    say(f"  worst rel-L2 over the rounds {worst}; checkpoint after the flush {ck:.2e}")
+    record_margin(f"chain/{dtype}_d{D}_cap{cap}", tol=tol, checkpoint=ck, **worst)
+    assert ck <= tol
+    assert int(cr.hist_len[1 - cr.cur].abs().sum()) == 0
+
+
+def test_bad_accepted_count_is_reported():
+    from tree_forked_gated_amd import binding as B
+    rng = np.random.default_rng(7)
+    n_seq, N, H, D = 3, 4, 2, 64
+    S0 = W._init(rng, n_seq, H, D, D, True)
+    cr = B.ChainRounds(torch.from_numpy(S0).cuda(), N, 8, torch.float32, keep_state=True)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().contiguous()
+    draft = {kk: f(x) for kk, x in _draft(rng, n_seq, N, H, D, "f32").items()}
+    cr.step(draft, torch.zeros(n_seq, dtype=torch.int32, device="cuda"), check=True)
+    cr.state.fill_(7.0)
+    with pytest.raises(B.GdnDeviceError) as ei:
+        cr.step(draft, torch.tensor([1, N + 1, 0], dtype=torch.int32, device="cuda"), check=True)
+    assert ei.value.code == 9 and ei.value.index == 1
+    assert bool((cr.state[1] == 7.0).all())  # the bad sequence is skipped

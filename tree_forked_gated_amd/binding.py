@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libgdn_tree.so")
 
 GDN_F32, GDN_BF16 = 0, 1
 DEV_ERRORS = {0: "ok", 1: "seq_start", 2: "parent order", 3: "parent in another sequence", 4: "fork capacity",
-              5: "level capacity", 6: "rows", 7: "commit path", 8: "workspace not planned for these sizes"}
+              5: "level capacity", 6: "rows", 7: "commit path", 8: "workspace not planned for these sizes",
+              9: "accepted count or history length out of range"}
 CHUNK = 64
 FWD_PLANNED = 1  # gdn_tree.h GDN_FWD_PLANNED: reuse the metadata already in the workspace
 
@@ -75,7 +76,7 @@ class Layout(ctypes.Structure):
 EXPORTS = ["gdn_tree_workspace_size", "gdn_tree_plan_layout", "gdn_tree_commit_workspace_size", "gdn_tree_plan",
            "gdn_tree_forward", "gdn_tree_forward_static", "gdn_tree_commit", "gdn_tree_check_error",
            "gdn_tree_strerror", "gdn_tree_last_error", "gdn_tree_version", "gdn_tree_attention_workspace_size",
-           "gdn_tree_attention"]
+           "gdn_tree_attention", "gdn_chain_step"]
 STATIC_WORKSPACE_BYTES = 64 << 20  # gdn_tree.h GDN_TREE_STATIC_WORKSPACE_BYTES
 
 
@@ -91,7 +92,7 @@ def _load():
     lib.gdn_tree_commit_workspace_size.restype = ctypes.c_size_t
     for name in ["gdn_tree_workspace_size", "gdn_tree_plan_layout", "gdn_tree_plan", "gdn_tree_forward",
                  "gdn_tree_forward_static", "gdn_tree_commit", "gdn_tree_check_error", "gdn_tree_version",
-                 "gdn_tree_attention_workspace_size", "gdn_tree_attention"]:
+                 "gdn_tree_attention_workspace_size", "gdn_tree_attention", "gdn_chain_step"]:
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -404,6 +405,76 @@ def attention(q, k, v, parent_idx, seq_start, *, max_levels, scale=None, workspa
     if check:
         raise_device_error(workspace, stream)
     return out, workspace
+
+
+# ------------------------------------------------------------- chain rounds
+
+class ChainDims(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int32), ("N", ctypes.c_int32), ("H", ctypes.c_int32), ("Dk", ctypes.c_int32),
+                ("Dv", ctypes.c_int32), ("dtype", ctypes.c_int32), ("hist_cap", ctypes.c_int32)]
+
+
+class ChainArgs(ctypes.Structure):
+    _fields_ = [("dims", ChainDims)] + [(f, ctypes.c_void_p) for f in (
+        "ckpt", "hist_pv", "hist_k", "hist_g", "hist_len_in", "hist_len_out", "prev_pv", "prev_k", "prev_g",
+        "accepted", "q", "k", "v", "log_gate", "beta", "out", "pseudo_v", "state_out", "workspace")] + [
+        ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32)]
+
+
+CHAIN_FLUSH = 1  # gdn_tree.h GDN_CHAIN_FLUSH
+
+
+class ChainRounds:
+    """Device buffers of speculative chain rounds for n_seq sequences and
+    gdn_chain_step over them (argument marshalling and buffer alternation only;
+    the commit and the verify run in the library's kernel).
+
+    ``step(draft, accepted)`` verifies a draft (dict of q, k, v, log_gate, beta
+    tensors [n_seq, N, H, D]) after accepting ``accepted`` (device int32
+    [n_seq]) tokens of the previous draft, and returns (out, pseudo_v) views of
+    the current draft buffers. ``state_out`` of the call receives the state each
+    round starts from when ``keep_state`` is set."""
+
+    def __init__(self, init_state, N, hist_cap, dtype, *, keep_state=False):
+        dev = init_state.device
+        n_seq, H, Dv, Dk = init_state.shape
+        self.dims = ChainDims(n_seq, N, H, Dk, Dv, _dtype_code(dtype), hist_cap)
+        self.ckpt = init_state.clone()
+        cap = max(1, hist_cap)
+        self.hist_pv = torch.zeros((n_seq, cap, H, Dv), dtype=torch.float32, device=dev)
+        self.hist_k = torch.zeros((n_seq, cap, H, Dk), dtype=dtype, device=dev)
+        self.hist_g = torch.zeros((n_seq, cap, H), dtype=torch.float32, device=dev)
+        self.hist_len = [torch.zeros(n_seq, dtype=torch.int32, device=dev) for _ in range(2)]
+        self.pv = [torch.zeros((n_seq, N, H, Dv), dtype=torch.float32, device=dev) for _ in range(2)]
+        self.k = [torch.zeros((n_seq, N, H, Dk), dtype=dtype, device=dev) for _ in range(2)]
+        self.g = [torch.zeros((n_seq, N, H), dtype=dtype, device=dev) for _ in range(2)]
+        self.out = [torch.zeros((n_seq, N, H, Dv), dtype=dtype, device=dev) for _ in range(2)]
+        self.state = torch.zeros_like(init_state) if keep_state else None
+        self.workspace = torch.empty(int(lib.gdn_tree_commit_workspace_size()), dtype=torch.uint8, device=dev)
+        self.cur = 0  # which draft buffers the next round writes
+
+    def step(self, draft, accepted, *, flush=False, stream=None, check=False):
+        c, p = self.cur, 1 - self.cur
+        self.k[c].copy_(draft["k"])
+        self.g[c].copy_(draft["log_gate"])
+        a = ChainArgs()
+        a.dims = self.dims
+        a.ckpt, a.hist_pv, a.hist_k, a.hist_g = _ptr(self.ckpt), _ptr(self.hist_pv), _ptr(self.hist_k), _ptr(self.hist_g)
+        a.hist_len_in, a.hist_len_out = _ptr(self.hist_len[p]), _ptr(self.hist_len[c])
+        a.prev_pv, a.prev_k, a.prev_g = _ptr(self.pv[p]), _ptr(self.k[p]), _ptr(self.g[p])
+        a.accepted = _ptr(accepted)
+        a.q, a.k, a.v = _ptr(draft["q"]), _ptr(self.k[c]), _ptr(draft["v"])
+        a.log_gate, a.beta = _ptr(self.g[c]), _ptr(draft["beta"])
+        a.out, a.pseudo_v = _ptr(self.out[c]), _ptr(self.pv[c])
+        a.state_out = _ptr(self.state)
+        a.workspace = _ptr(self.workspace)
+        a.workspace_bytes = self.workspace.numel()
+        a.flags = CHAIN_FLUSH if flush else 0
+        _check(lib.gdn_chain_step(ctypes.byref(a), _stream(stream)), "gdn_chain_step")
+        if check:
+            raise_device_error(self.workspace, stream)
+        self.cur = p
+        return self.out[c], self.pv[c]
 
 
 # -------------------------------------------------------------------- commit

@@ -217,6 +217,7 @@ const char* gdn_tree_strerror(int code) {
     case 100 + GDN_DEV_ROWS: return "an out/state row is out of range or repeated";
     case 100 + GDN_DEV_PATH: return "a commit path is not a root-to-node parent chain";
     case 100 + GDN_DEV_NOT_PLANNED: return "GDN_FWD_PLANNED on a workspace without a matching plan";
+    case 100 + GDN_DEV_CHAIN: return "an accepted count or history length is out of range";
     default: return "unknown code";
   }
 }
@@ -360,6 +361,34 @@ int gdn_tree_attention(const gdn_attn_args* a, void* stream) {
   if (a->workspace_bytes < A.total) return fail(GDN_ERR_WORKSPACE, "workspace smaller than gdn_tree_attention_workspace_size");
   hipError_t e = launch_attention(*a, A, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "gdn_tree_attention");
+  return GDN_OK;
+}
+
+int gdn_chain_step(const gdn_chain_args* a, void* stream) {
+  if (!a) return fail(GDN_ERR_NULL, "args is NULL");
+  const gdn_chain_dims& d = a->dims;
+  if (d.dtype != GDN_F32 && d.dtype != GDN_BF16) return fail(GDN_ERR_DTYPE, "dtype must be GDN_F32 or GDN_BF16");
+  if (d.n_seq < 0 || d.H < 1 || d.N < 1 || d.N > 32 || d.hist_cap < 0)
+    return fail(GDN_ERR_DIMS, "n_seq >= 0, H >= 1, N in [1, 32] and hist_cap >= 0 are required");
+  if (!(d.Dk == 32 || d.Dk == 64 || d.Dk == 128) || d.Dv < 16 || d.Dv > 128 || d.Dv % 16)
+    return fail(GDN_ERR_DIMS, "Dk must be 32, 64 or 128 and Dv a multiple of 16 up to 128");
+  if ((long long)d.H * (d.Dk > d.Dv ? d.Dk : d.Dv) >= (1ll << 24))
+    return fail(GDN_ERR_DIMS, "H * max(Dk, Dv) must stay below 2^24");
+  if (d.n_seq > 0) {
+    if (!a->ckpt || !a->hist_len_in || !a->hist_len_out || !a->prev_pv || !a->prev_k || !a->prev_g || !a->accepted ||
+        !a->q || !a->k || !a->v || !a->log_gate || !a->beta || !a->out || !a->pseudo_v || !a->workspace)
+      return fail(GDN_ERR_NULL, "a required pointer of gdn_chain_step is NULL");
+    if (d.hist_cap > 0 && (!a->hist_pv || !a->hist_k || !a->hist_g))
+      return fail(GDN_ERR_NULL, "hist_pv, hist_k and hist_g are required when hist_cap > 0");
+    if ((const void*)a->hist_len_in == (const void*)a->hist_len_out || (const void*)a->prev_pv == (const void*)a->pseudo_v)
+      return fail(GDN_ERR_ARGS, "hist_len_out and pseudo_v must be other buffers than hist_len_in and prev_pv");
+    if (!aligned16(a->ckpt) || !aligned16(a->state_out))
+      return fail(GDN_ERR_ARGS, "ckpt and state_out must be 16-byte aligned");
+    if (a->workspace_bytes < 8) return fail(GDN_ERR_WORKSPACE, "the chain workspace holds an 8-byte error word");
+  }
+  if (a->flags & ~GDN_CHAIN_FLUSH) return fail(GDN_ERR_ARGS, "unknown flags");
+  hipError_t e = launch_chain(*a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail_hip(e, "gdn_chain_step");
   return GDN_OK;
 }
 

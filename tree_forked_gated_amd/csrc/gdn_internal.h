@@ -106,4 +106,8 @@ bool attn_layout(const gdn_attn_dims& d, AttnLayout* A);
 hipError_t launch_attention(const gdn_attn_args& a, const AttnLayout& A, hipStream_t s);
 int attn_max_spans();
 
+// Fused chain round (chain.hip).
+hipError_t launch_chain(const gdn_chain_args& c, hipStream_t s);
+int chain_dyn_lds(int N, int dk);
+
 }  // namespace gdn
