@@ -145,6 +145,9 @@ def main():
                     help="also time whole steps replayed from captured graphs (one per input set)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (calibrates memory counters)")
+    ap.add_argument("--attention", action="store_true",
+                    help="time ForkAttention (gdn_tree_attention) over the workload's structure instead of the "
+                         "recurrence: 16 query heads over 2 key/value heads, d 128, bf16")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -152,6 +155,8 @@ def main():
         print(f"bench.py runs on one GPU only: the tree-GDN path has no multi-GPU mode in this library "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr, flush=True)
         sys.exit(2)
+    if args.attention:
+        return attention_main(args)
 
     import torch
     from tree_forked_gated_amd import binding as B
@@ -447,6 +452,132 @@ def main():
         line["graph_replay"] = graph
     if mfma_probe is not None:
         line["mfma_probe"] = mfma_probe
+    print(json.dumps(line), flush=True)
+
+
+# ------------------------------------------------------------------ attention
+
+ATTN_METRIC = "ForkAttention tokens/s on 1 MI355X; fraction of bf16 MFMA roofline"
+ATTN_HQ, ATTN_HKV, ATTN_D = 16, 2, 128
+
+
+def attention_counts(parent, T, Hq=ATTN_HQ, D=ATTN_D, Hkv=ATTN_HKV, es=2):
+    """Flops of one ForkAttention call: for every query head and token,
+    q . k over its visible keys and the weighted sum of their values,
+    2 D flops each: 4 D Hq sum over tokens of |ancestors-or-self|. Bytes: q,
+    k, v read once and out written once."""
+    depth = np.zeros(T, np.int64)
+    for t in range(T):
+        p = parent[t]
+        depth[t] = depth[p] + 1 if p >= 0 else 0
+    visible = int(np.sum(depth + 1))
+    return {"flops": float(4 * D * Hq * visible), "visible": visible,
+            "bytes": float(T * (2 * Hq + 2 * Hkv) * D * es)}
+
+
+def attention_main(args):
+    import torch
+    from tree_forked_gated_amd import binding as B
+    from tree_forked_gated_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    name = args.workload
+    st = W.get(name, H=1, D=16)  # structure only; values below
+    parent, seq_start = st.parent, st.seq_start
+    T = st.T
+    cap = B.capacities(parent, seq_start)
+    rng = np.random.default_rng(2000)
+    q = W.bf16_round(W._normal_f32(rng, (T, ATTN_HQ, ATTN_D), unit_rows=True))
+    k = W.bf16_round(W._normal_f32(rng, (T, ATTN_HKV, ATTN_D), unit_rows=True))
+    v = W.bf16_round(W._normal_f32(rng, (T, ATTN_HKV, ATTN_D)))
+    cnt = attention_counts(parent, T)
+    log(f"attention over {st.name} structure: T={T} Hq={ATTN_HQ} Hkv={ATTN_HKV} D={ATTN_D}, "
+        f"{cnt['visible']} visible (token, key) pairs, {cnt['flops'] / 1e12:.3f} TFLOP per call")
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(torch.bfloat16)
+    base = {"q": f(q), "k": f(k), "v": f(v)}
+    sets = [base] + [{kk: t.clone() for kk, t in base.items()} for _ in range(max(1, args.rotate) - 1)]
+    par_d = torch.from_numpy(parent.astype(np.int32)).to(dev)
+    seq_d = torch.from_numpy(seq_start.astype(np.int32)).to(dev)
+    scale = ATTN_D ** -0.5
+    for x in sets:
+        x["out"], x["ws"] = B.attention(x["q"], x["k"], x["v"], par_d, seq_d, max_levels=cap["max_levels"],
+                                        scale=scale, stream=stream)
+    torch.cuda.synchronize()
+    for x in sets:
+        B.raise_device_error(x["ws"], stream)
+
+    def step(i, planned):
+        x = sets[i % len(sets)]
+        B.attention(x["q"], x["k"], x["v"], par_d, seq_d, max_levels=cap["max_levels"], scale=scale,
+                    workspace=x["ws"], out=x["out"], planned=planned, stream=stream)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step(i, False)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    ms_step = float(per.mean())
+    # the attention kernel alone (metadata reused): the dominant kernel's launch duration
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i, True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_kern = e0.elapsed_time(e1) / args.steps
+    for x in sets:
+        B.raise_device_error(x["ws"], stream)
+    tf = cnt["flops"] / (ms_kern * 1e-3) / 1e12
+    log(f"attention: {ms_step:.4f} ms/step, kernel {ms_kern:.4f} ms ({tf:.1f} TFLOP/s)")
+    roof = {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "k_fork_attn",
+            "launch_unit": "one attention call (metadata reused)", "ms_per_step": round(ms_kern, 5),
+            "alg_flops": cnt["flops"], "alg_bytes": cnt["bytes"]}
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        from oracle.attention import fork_attention
+        out = sets[0]["out"].float().cpu().numpy()
+        rows_all = np.unique(np.concatenate([rng.integers(0, T, 64), [T - 1]]))
+        t0 = time.perf_counter()
+        n_rows, ref_rows, refs = 0, [], []
+        while n_rows == 0 or time.perf_counter() - t0 < args.cpu_min_s:
+            r = rows_all[n_rows % rows_all.shape[0]: n_rows % rows_all.shape[0] + 8]
+            refs.append(fork_attention(q, k, v, parent, seq_start, scale, rows=r))
+            ref_rows.append(r)
+            n_rows += r.shape[0]
+            if n_rows >= 4 * rows_all.shape[0]:
+                break
+        cpu_s = time.perf_counter() - t0
+        rr = np.concatenate(ref_rows)
+        ref = np.concatenate(refs)
+        vis_rows = float(np.mean([len(W.root_path(parent, int(t))) for t in rr]))
+        cpu_tok_s = n_rows / cpu_s * (cnt["visible"] / T) / vis_rows  # rows/s scaled to the stream's mean visible keys
+        cpu = {"value": round(cpu_tok_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n_rows} rows of {name} (mean {vis_rows:.0f} visible keys) through the fp64 per-token "
+                         f"oracle in {cpu_s:.2f} s on 1 thread, scaled to the stream's mean of "
+                         f"{cnt['visible'] / T:.0f} visible keys per token"}
+        g = out[rr].astype(np.float64)
+        parity = {"out": float(f"{np.linalg.norm(g - ref) / np.linalg.norm(ref):.3e}"), "tol": 1e-2,
+                  "rows": int(rr.shape[0])}
+        parity["ok"] = parity["out"] <= 1e-2
+        log(f"cpu baseline: {n_rows} rows in {cpu_s:.2f} s; parity {parity}")
+    line = {"metric": ATTN_METRIC, "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"attention_{st.name.split('_h')[0]}", "tokens": T, "q_heads": ATTN_HQ,
+                       "kv_heads": ATTN_HKV, "d": ATTN_D, "sequences": st.n_seq, "chunk": CHUNK,
+                       "parallelism": "single GPU", "input_sets_rotated": len(sets)},
+            "roofline": roof, "cpu_baseline": cpu, "parity_vs_oracle": parity,
+            "step_ms_percentiles": {"p10": round(float(np.percentile(per, 10)), 5),
+                                    "p50": round(float(np.median(per)), 5),
+                                    "p90": round(float(np.percentile(per, 90)), 5)}}
     print(json.dumps(line), flush=True)
 
 
