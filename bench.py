@@ -145,6 +145,9 @@ def main():
                     help="also time whole steps replayed from captured graphs (one per input set)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (calibrates memory counters)")
+    ap.add_argument("--chain", action="store_true",
+                    help="time speculative chain rounds (gdn_chain_step): 64 sequences x 32 heads x d 128, "
+                         "4-token drafts, with the state written every round and with a 16-token deferred history")
     ap.add_argument("--attention", action="store_true",
                     help="time ForkAttention (gdn_tree_attention) over the workload's structure instead of the "
                          "recurrence: 16 query heads over 2 key/value heads, d 128, bf16")
@@ -157,6 +160,8 @@ def main():
         sys.exit(2)
     if args.attention:
         return attention_main(args)
+    if args.chain:
+        return chain_main(args)
 
     import torch
     from tree_forked_gated_amd import binding as B
@@ -578,6 +583,111 @@ def attention_main(args):
             "step_ms_percentiles": {"p10": round(float(np.percentile(per, 10)), 5),
                                     "p50": round(float(np.median(per)), 5),
                                     "p90": round(float(np.percentile(per, 90)), 5)}}
+    print(json.dumps(line), flush=True)
+
+
+# --------------------------------------------------------------- chain rounds
+
+CHAIN_METRIC = "speculative chain rounds: draft tokens verified per second on 1 MI355X; fraction of HBM roofline"
+
+
+def chain_round_bytes(acc_rounds, N, H, Dk, Dv, cap, es=2):
+    """HBM bytes of each round of gdn_chain_step for the given accepted counts
+    (rows: rounds; accepted[r] is what round r commits), replaying the flush
+    rule: every round reads the checkpoint, the history and the accepted
+    prefix of the previous draft, reads the new draft and writes its outputs
+    and pseudo-values; it then writes the state (a flush) or appends the
+    accepted tokens to the history."""
+    n_seq = acc_rounds.shape[1]
+    hl = np.zeros(n_seq, np.int64)
+    out = []
+    state = Dv * Dk * 4
+    row_pv, row_k, row_g = Dv * 4, Dk * es, 4
+    for acc in acc_rounds:
+        L = hl + acc
+        flush = (L > cap) if cap > 0 else (L > 0)
+        b = n_seq * state + np.sum(hl) * (row_pv + row_k + row_g) + np.sum(acc) * (row_pv + row_k + es)
+        b += n_seq * N * ((2 * Dk + Dv + 2) * es + Dv * (es + 4))
+        b += np.sum(flush) * state + np.sum(np.where(flush, 0, acc)) * (row_pv + row_k + row_g)
+        out.append(float(b) * H)
+        hl = np.where(flush, 0, L)
+    return np.array(out)
+
+
+def chain_main(args):
+    import torch
+    from tree_forked_gated_amd import binding as B
+    from tree_forked_gated_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    n_seq, N, H, D, R = 64, 4, 32, 128, 48
+    rng = np.random.default_rng(3000)
+    S0 = W._init(rng, n_seq, H, D, D, True)
+    drafts = []
+    for _ in range(3):
+        q, k, v, beta, g = W._values(rng, n_seq * N, H, D, D, "bf16")
+        sh = lambda a: torch.from_numpy(np.ascontiguousarray(a.reshape((n_seq, N) + a.shape[1:]), np.float32)).to(
+            dev).to(torch.bfloat16).contiguous()
+        drafts.append({"q": sh(q), "k": sh(k), "v": sh(v), "beta": sh(beta), "log_gate": sh(g)})
+    acc = rng.integers(0, N + 1, (R, n_seq))
+    acc_d = [torch.from_numpy(a.astype(np.int32)).to(dev) for a in acc]
+    results = {}
+    for cap in (0, 16):
+        cr = B.ChainRounds(torch.from_numpy(S0).to(dev), N, cap, torch.bfloat16)
+        for i in range(args.warmup):
+            cr.step(drafts[i % 3], acc_d[i % R])
+        torch.cuda.synchronize()
+        cr = B.ChainRounds(torch.from_numpy(S0).to(dev), N, cap, torch.bfloat16)  # restart from the initial state
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
+        evs[0].record(stream)
+        for r in range(R):
+            cr.step(drafts[r % 3], acc_d[r - 1] if r else torch.zeros_like(acc_d[0]), stream=stream)
+            evs[r + 1].record(stream)
+        torch.cuda.synchronize()
+        B.raise_device_error(cr.workspace, stream)
+        per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(R)])
+        prev = np.concatenate([np.zeros((1, n_seq), np.int64), acc[:-1]])
+        byt = chain_round_bytes(prev, N, H, D, D, cap)
+        results[cap] = {"ms_per_round": float(per.mean()), "bytes_per_round": float(byt.mean()),
+                        "gbs": float(byt.sum() / (per.sum() * 1e-3) / 1e9), "per": per}
+        log(f"chain rounds, history capacity {cap}: {per.mean() * 1e3:.1f} us/round, "
+            f"{byt.mean() / 1e6:.1f} MB/round, {results[cap]['gbs']:.0f} GB/s")
+    # the bench line: the deferred write (history of 16 tokens); the copy before each step is the
+    # binding keeping this round's keys and gates for the next one
+    d = results[16]
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        from oracle.chain import chain_rounds
+        sub = 4  # sequences in the CPU sample
+        host = [{kk: x[:sub].float().cpu().numpy() for kk, x in dr.items()} for dr in drafts]
+        t0 = time.perf_counter()
+        rounds_done = 0
+        while rounds_done == 0 or time.perf_counter() - t0 < min(args.cpu_min_s, 10.0):
+            chain_rounds(S0[:sub], [host[r % 3] for r in range(4)], [acc[r][:sub] for r in range(4)])
+            rounds_done += 4
+        cpu_s = time.perf_counter() - t0
+        cpu = {"value": round(rounds_done * sub * N / cpu_s, 2), "unit": "draft tokens/s", "cores": 1,
+               "kind": "oracle", "sample": f"{rounds_done} rounds of {sub} sequences x {H} heads (fp64 per-token "
+                                           f"chain oracle, numpy) in {cpu_s:.2f} s on 1 thread"}
+    line = {"metric": CHAIN_METRIC, "value": round(n_seq * N / (d["ms_per_round"] * 1e-3), 1),
+            "unit": "draft tokens/s", "n_gpus": 1, "steps": R, "warmup": args.warmup,
+            "ms_per_step": round(d["ms_per_round"], 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"chain_rounds_{n_seq}x{N}_h{H}_d{D}", "sequences": n_seq, "draft_tokens": N,
+                       "heads": H, "d_k": D, "d_v": D, "history_capacity": 16, "accepted": "uniform 0..4",
+                       "parallelism": "single GPU"},
+            "roofline": {"bound": "hbm", "achieved": round(d["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_chain_step",
+                         "launch_unit": "one round", "alg_bytes": d["bytes_per_round"]},
+            "state_every_round": {"ms_per_round": round(results[0]["ms_per_round"], 5),
+                                  "bytes_per_round": results[0]["bytes_per_round"],
+                                  "hbm_frac": round(results[0]["gbs"] / HBM_PEAK_GBS, 4)},
+            "cpu_baseline": cpu, "parity_vs_oracle": parity,
+            "step_ms_percentiles": {"p10": round(float(np.percentile(d["per"], 10)), 5),
+                                    "p50": round(float(np.median(d["per"])), 5),
+                                    "p90": round(float(np.percentile(d["per"], 90)), 5)}}
     print(json.dumps(line), flush=True)
 
 

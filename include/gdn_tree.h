@@ -319,7 +319,7 @@ typedef struct gdn_attn_dims {
 
 /*
  * Arguments of gdn_tree_attention.
- *  scale                     softmax scale (commonly 1 / sqrt(D))
+ *  scale                     softmax scale, positive and finite (commonly 1 / sqrt(D))
  *  q [T, Hq, D], k and v [T, Hkv, D]   bf16, token-major, 16-byte aligned
  *  parent_idx [T], seq_start [n_seq + 1]   the stream's structure, as for gdn_tree_forward
  *  out [T, Hq, D]            bf16, 16-byte aligned

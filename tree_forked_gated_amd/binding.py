@@ -430,10 +430,12 @@ class ChainRounds:
     the commit and the verify run in the library's kernel).
 
     ``step(draft, accepted)`` verifies a draft (dict of q, k, v, log_gate, beta
-    tensors [n_seq, N, H, D]) after accepting ``accepted`` (device int32
-    [n_seq]) tokens of the previous draft, and returns (out, pseudo_v) views of
-    the current draft buffers. ``state_out`` of the call receives the state each
-    round starts from when ``keep_state`` is set."""
+    tensors [n_seq, N, H, D], contiguous) after accepting ``accepted`` (device
+    int32 [n_seq]) tokens of the previous draft, and returns (out, pseudo_v)
+    views of the current draft buffers. The draft's k and log_gate tensors are
+    the next step's prev_k and prev_g: keep them unchanged until then.
+    ``state_out`` of the call receives the state each round starts from when
+    ``keep_state`` is set."""
 
     def __init__(self, init_state, N, hist_cap, dtype, *, keep_state=False):
         dev = init_state.device
@@ -446,8 +448,9 @@ class ChainRounds:
         self.hist_g = torch.zeros((n_seq, cap, H), dtype=torch.float32, device=dev)
         self.hist_len = [torch.zeros(n_seq, dtype=torch.int32, device=dev) for _ in range(2)]
         self.pv = [torch.zeros((n_seq, N, H, Dv), dtype=torch.float32, device=dev) for _ in range(2)]
-        self.k = [torch.zeros((n_seq, N, H, Dk), dtype=dtype, device=dev) for _ in range(2)]
-        self.g = [torch.zeros((n_seq, N, H), dtype=dtype, device=dev) for _ in range(2)]
+        # the previous draft's keys and log gates (zeros before the first round)
+        self.prev_k = torch.zeros((n_seq, N, H, Dk), dtype=dtype, device=dev)
+        self.prev_g = torch.zeros((n_seq, N, H), dtype=dtype, device=dev)
         self.out = [torch.zeros((n_seq, N, H, Dv), dtype=dtype, device=dev) for _ in range(2)]
         self.state = torch.zeros_like(init_state) if keep_state else None
         self.workspace = torch.empty(int(lib.gdn_tree_commit_workspace_size()), dtype=torch.uint8, device=dev)
@@ -455,16 +458,14 @@ class ChainRounds:
 
     def step(self, draft, accepted, *, flush=False, stream=None, check=False):
         c, p = self.cur, 1 - self.cur
-        self.k[c].copy_(draft["k"])
-        self.g[c].copy_(draft["log_gate"])
         a = ChainArgs()
         a.dims = self.dims
         a.ckpt, a.hist_pv, a.hist_k, a.hist_g = _ptr(self.ckpt), _ptr(self.hist_pv), _ptr(self.hist_k), _ptr(self.hist_g)
         a.hist_len_in, a.hist_len_out = _ptr(self.hist_len[p]), _ptr(self.hist_len[c])
-        a.prev_pv, a.prev_k, a.prev_g = _ptr(self.pv[p]), _ptr(self.k[p]), _ptr(self.g[p])
+        a.prev_pv, a.prev_k, a.prev_g = _ptr(self.pv[p]), _ptr(self.prev_k), _ptr(self.prev_g)
         a.accepted = _ptr(accepted)
-        a.q, a.k, a.v = _ptr(draft["q"]), _ptr(self.k[c]), _ptr(draft["v"])
-        a.log_gate, a.beta = _ptr(self.g[c]), _ptr(draft["beta"])
+        a.q, a.k, a.v = _ptr(draft["q"]), _ptr(draft["k"]), _ptr(draft["v"])
+        a.log_gate, a.beta = _ptr(draft["log_gate"]), _ptr(draft["beta"])
         a.out, a.pseudo_v = _ptr(self.out[c]), _ptr(self.pv[c])
         a.state_out = _ptr(self.state)
         a.workspace = _ptr(self.workspace)
@@ -473,6 +474,7 @@ class ChainRounds:
         _check(lib.gdn_chain_step(ctypes.byref(a), _stream(stream)), "gdn_chain_step")
         if check:
             raise_device_error(self.workspace, stream)
+        self.prev_k, self.prev_g = draft["k"], draft["log_gate"]
         self.cur = p
         return self.out[c], self.pv[c]
 

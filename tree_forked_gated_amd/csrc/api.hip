@@ -354,8 +354,7 @@ int gdn_tree_attention(const gdn_attn_args* a, void* stream) {
     return fail(GDN_ERR_ARGS, "q, k, v and out must be 16-byte aligned");
   if (((uintptr_t)a->workspace & 255u) != 0) return fail(GDN_ERR_ARGS, "workspace must be 256-byte aligned");
   if (a->flags & ~GDN_ATTN_PLANNED) return fail(GDN_ERR_ARGS, "unknown flags");
-  if (!(a->scale == a->scale) || a->scale > 3.0e38f || a->scale < -3.0e38f)
-    return fail(GDN_ERR_ARGS, "scale must be finite");
+  if (!(a->scale > 0.f) || a->scale > 3.0e38f) return fail(GDN_ERR_ARGS, "scale must be positive and finite");
   AttnLayout A;
   if (!attn_layout(d, &A)) return fail(GDN_ERR_DIMS, "bad sizes");
   if (a->workspace_bytes < A.total) return fail(GDN_ERR_WORKSPACE, "workspace smaller than gdn_tree_attention_workspace_size");

@@ -22,11 +22,13 @@
 // shapes depend only on the sizes.
 //
 // The attention kernel is a persistent grid of 4-wave workgroups that claim
-// (chunk, query head) items. Each wave owns 16 queries and walks the item's key
-// tiles of 64 keys with an online softmax: S^T = K Q^T and O^T += V^T P^T on
-// 16x16x32 bf16 matrix cores, fp32 softmax state. K and V tiles are copied
-// straight from HBM into LDS one tile ahead (double-buffered). Fully visible
-// tiles take no mask.
+// (chunk, query heads) items: two query heads of one key/value group per item
+// when the group has an even number of them, so that every K and V fragment
+// read from LDS feeds two matrix products. Each wave owns 16 queries and walks
+// the item's key tiles of 64 keys with an online softmax: S^T = K Q^T and
+// O^T += V^T P^T on 16x16x32 bf16 matrix cores, fp32 softmax state. K and V
+// tiles are copied straight from HBM into LDS one tile ahead
+// (double-buffered). Fully visible tiles take no mask.
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -61,7 +63,7 @@ struct AttnArgs {
   const int* n_items;
   int* claim;
   int Hq, Hkv, max_levels;
-  float c;  // scale * log2(e)
+  float c;  // scale * log2(e), positive
 };
 
 __device__ __forceinline__ void dma16(const void* sbase, unsigned voff, uint32_t lds_addr) {
@@ -137,6 +139,9 @@ __device__ __forceinline__ Tile next_tile(const int2* sps, int nsp, int sp, int 
   return t;
 }
 
+// HPW query heads of one key/value group per wave: every K and V fragment read
+// from LDS feeds HPW matrix products.
+template <int HPW>
 __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_claim;
@@ -145,9 +150,10 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
   const int g4 = lane >> 4, l16 = lane & 15;
   if (*a.err != kNoError) return;  // structural error in the tree: nothing is computed
   const int n_items = *a.n_items;
-  const long long total = (long long)n_items * a.Hq;
+  const int HG = a.Hq / HPW;  // head groups of HPW query heads
+  const long long total = (long long)n_items * HG;
   const int G = a.Hq / a.Hkv;
-  const unsigned rs_q = (unsigned)a.Hq * (D * 2), rs_kv = (unsigned)a.Hkv * (D * 2);
+  const unsigned rs_kv = (unsigned)a.Hkv * (D * 2);
   int2* sps = reinterpret_cast<int2*>(smem + oSp);
   // A-operand rows of the K fragments (row l16 of a 16-key block, d 32 ks + 8 g4 .. + 7)
   int oF[4];
@@ -169,24 +175,27 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
     __syncthreads();
     const long long idx = s_claim;
     if (idx >= total) break;
-    const int item = (int)(idx / a.Hq), h = (int)(idx % a.Hq);
-    const int hk = h / G;
+    const int item = (int)(idx / HG), h0 = (int)(idx % HG) * HPW;
+    const int hk = h0 / G;
     const int4 inf = a.item_info[item];
     const int q0 = rfl(inf.x), nq = rfl(inf.y), tree = rfl(inf.z & 1), sq = rfl(inf.z >> 1);
     const int nsp = rfl(min(inf.w, kMaxSpans));
     if (tid < nsp) sps[tid] = a.spans[(size_t)item * a.max_levels + tid];
-    // this wave's 16 queries as MFMA fragments (zero past the chunk's queries)
+    // this wave's 16 queries of each head as MFMA fragments (zero past the chunk's queries)
     const int qi = 16 * w + l16;  // query within the chunk
-    bf16x8 Qf[4];
+    bf16x8 Qf[HPW][4];
     unsigned long long tmask = 0;
     {
       const bool ok = qi < nq;
-      const __bf16* qrow = a.q + ((size_t)(q0 + (ok ? qi : 0)) * a.Hq + h) * D;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g4);
-        if (!ok) x = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-        Qf[ks] = x;
+      for (int j = 0; j < HPW; ++j) {
+        const __bf16* qrow = a.q + ((size_t)(q0 + (ok ? qi : 0)) * a.Hq + h0 + j) * D;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * g4);
+          if (!ok) x = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+          Qf[j][ks] = x;
+        }
       }
       if (tree && ok) tmask = a.tree_mask[(size_t)sq * kT + qi];
     }
@@ -200,10 +209,15 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
     }
     wait_vm();
     lds_barrier();
-    f32x4 O[8];
+    f32x4 O[HPW][8];
+    float m[HPW], l[HPW];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) O[dt] = zero;
-    float m = -INFINITY, l = 0.f;
+    for (int j = 0; j < HPW; ++j) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) O[j][dt] = zero;
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+    }
     const bool active = 16 * w < nq;
     for (int it = 0; cur.valid; ++it) {
       const Tile nxt = next_tile(sps, nsp, cur.sp, cur.k0 + kT, q0, tree);
@@ -216,68 +230,93 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
         const unsigned char* kt = smem + oK + b * kTileB;
         const unsigned char* vt = smem + oV + b * kTileB;
         // S^T = K Q^T: lane (query l16, g4) holds keys 16 kb + 4 g4 + r
-        f32x4 S[4];
+        f32x4 S[HPW][4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          S[kb] = zero;
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            S[kb] = mma32(*reinterpret_cast<const bf16x8*>(kt + kb * 4096 + oF[ks]), Qf[ks], S[kb]);
+          for (int j = 0; j < HPW; ++j) S[j][kb] = zero;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + kb * 4096 + oF[ks]);
+#pragma unroll
+            for (int j = 0; j < HPW; ++j) S[j][kb] = mma32(kf, Qf[j][ks], S[j][kb]);
+          }
         }
-        float x[4][4];
-        float mt = -INFINITY;
+        bf16x8 w01[HPW], w23[HPW];
+        float alpha[HPW];
+        bool rescale[HPW];
+        // masks only where a tile is not fully visible (the diagonal tile, a span's last tile, tree tiles)
+        const bool masked = cur.kind != 0 || cur.n < kT;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int j = 0; j < HPW; ++j) {
+          if (masked) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int kk = 16 * kb + 4 * g4 + r;
-            bool ok = kk < cur.n;
-            if (cur.kind == 1) ok = ok && kk <= qi;
-            else if (cur.kind == 2) ok = ok && ((tmask >> kk) & 1ull);
-            x[kb][r] = ok ? S[kb][r] * a.c : -INFINITY;
-            mt = fmaxf(mt, x[kb][r]);
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int kk = 16 * kb + 4 * g4 + r;
+                bool ok = kk < cur.n;
+                if (cur.kind == 1) ok = ok && kk <= qi;
+                else if (cur.kind == 2) ok = ok && ((tmask >> kk) & 1ull);
+                if (!ok) S[j][kb][r] = -INFINITY;
+              }
           }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m, mt);
-        const float mref = mn == -INFINITY ? 0.f : mn;
-        const float alpha = __builtin_amdgcn_exp2f(m - mref);
-        f32x4 P[4];
-        float ls = 0.f;
+          // running maxima in the scaled log2 domain (scale > 0): m = c max(s)
+          float mt = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+          for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            P[kb][r] = __builtin_amdgcn_exp2f(x[kb][r] - mref);
-            ls += P[kb][r];
-          }
-        l = l * alpha + ls;
-        m = mn;
-        const bf16x8 w01 = cat8b(to_bf4(P[0]), to_bf4(P[1]));
-        const bf16x8 w23 = cat8b(to_bf4(P[2]), to_bf4(P[3]));
+            for (int r = 0; r < 4; ++r) mt = fmaxf(mt, S[j][kb][r]);
+          mt = fmaxf(mt, __shfl_xor(mt, 16));
+          mt = fmaxf(mt, __shfl_xor(mt, 32));
+          const float mn = fmaxf(m[j], mt * a.c);
+          const float mref = mn == -INFINITY ? 0.f : mn;
+          alpha[j] = __builtin_amdgcn_exp2f(m[j] - mref);
+          rescale[j] = __builtin_amdgcn_ballot_w64(mn != m[j]) != 0ull;  // some query's maximum moved
+          float ls = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              S[j][kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[j][kb][r], a.c, -mref));
+              ls += S[j][kb][r];
+            }
+          l[j] = rescale[j] ? l[j] * alpha[j] + ls : l[j] + ls;
+          m[j] = mn;
+          w01[j] = cat8b(to_bf4(S[j][0]), to_bf4(S[j][1]));
+          w23[j] = cat8b(to_bf4(S[j][2]), to_bf4(S[j][3]));
+        }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           const unsigned char* vp = vt + oT[dt];
-          f32x4 o = O[dt];
+          const bf16x8 v01 = cat8(tr_read(vp), tr_read(vp + 4096));
+          const bf16x8 v23 = cat8(tr_read(vp + 8192), tr_read(vp + 12288));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] *= alpha;
-          o = mma32(cat8(tr_read(vp), tr_read(vp + 4096)), w01, o);
-          O[dt] = mma32(cat8(tr_read(vp + 8192), tr_read(vp + 12288)), w23, o);
+          for (int j = 0; j < HPW; ++j) {
+            f32x4 o = O[j][dt];
+            if (rescale[j]) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) o[r] *= alpha[j];
+            }
+            o = mma32(v01, w01[j], o);
+            O[j][dt] = mma32(v23, w23[j], o);
+          }
         }
       }
       wait_vm();  // the next tile has landed
       lds_barrier();
       cur = nxt;
     }
-    if (active) {
-      float lt = l + __shfl_xor(l, 16);
-      lt += __shfl_xor(lt, 32);
-      const float inv = 1.f / lt;
-      if (qi < nq) {
-        __bf16* orow = a.out + ((size_t)(q0 + qi) * a.Hq + h) * D;
+    if (active && qi < nq) {
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        float lt = l[j] + __shfl_xor(l[j], 16);
+        lt += __shfl_xor(lt, 32);
+        const float inv = 1.f / lt;
+        __bf16* orow = a.out + ((size_t)(q0 + qi) * a.Hq + h0 + j) * D;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          f32x4 o = O[dt];
+          f32x4 o = O[j][dt];
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[r] *= inv;
           *reinterpret_cast<bf16x4*>(orow + 32 * (dt >> 1) + 8 * g4 + 4 * (dt & 1)) = to_bf4(o);
@@ -449,12 +488,16 @@ hipError_t launch_attention(const gdn_attn_args& aa, const AttnLayout& A, hipStr
   x.Hkv = aa.dims.Hkv;
   x.max_levels = aa.dims.max_levels;
   x.c = aa.scale * kLog2e;
+  // two query heads per wave when a key/value group has an even number of them
+  const bool two = (aa.dims.Hq / aa.dims.Hkv) % 2 == 0;
+  const void* kern = two ? reinterpret_cast<const void*>(k_fork_attn<2>) : reinterpret_cast<const void*>(k_fork_attn<1>);
   int cus = 0, occ = 1;
-  e = ensure_dynamic_lds(reinterpret_cast<const void*>(k_fork_attn), kLds, kThr, &occ);
+  e = ensure_dynamic_lds(kern, kLds, kThr, &occ);
   if (e != hipSuccess) return e;
   e = current_device_cus(&cus);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_fork_attn, dim3(cus * occ), dim3(kThr), kLds, s, x);
+  if (two) hipLaunchKernelGGL(k_fork_attn<2>, dim3(cus * occ), dim3(kThr), kLds, s, x);
+  else hipLaunchKernelGGL(k_fork_attn<1>, dim3(cus * occ), dim3(kThr), kLds, s, x);
   return hipGetLastError();
 }
 
