@@ -20,6 +20,12 @@ heads, key/value head h // G):
     o_t = sum over j ancestor-or-self of t of softmax_j(scale * q_t . k_j) v_j
 
 plain per token, in fp64, walking the parent pointers. Small inputs only.
+
+Cached keys (section 3.4, incremental state forking: a checkpoint keeps the
+keys and values of the full-attention layers before its position, and a
+resumed request's tokens come after them). Sequence s may have cached rows
+[cache_start[s], cache_start[s + 1]) of k_cache and v_cache: they precede the
+sequence's roots, so every token of s sees all of them, before its root path.
 """
 from __future__ import annotations
 
@@ -50,14 +56,25 @@ def check_structure(parent: np.ndarray, seq_start: np.ndarray) -> None:
 
 
 def fork_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, parent: np.ndarray, seq_start: np.ndarray,
-                   scale: float, rows=None) -> np.ndarray:
+                   scale: float, rows=None, k_cache=None, v_cache=None, cache_start=None) -> np.ndarray:
     """Outputs [len(rows) or T, Hq, D] in fp64 for q [T, Hq, D], k and v
-    [T, Hkv, D]. rows: the tokens to compute (default: all), one by one."""
+    [T, Hkv, D]. rows: the tokens to compute (default: all), one by one.
+    k_cache, v_cache [Tc, Hkv, D] and cache_start [n_seq + 1]: optional
+    cached keys and values of each sequence."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     parent = np.asarray(parent, np.int64)
-    check_structure(parent, np.asarray(seq_start, np.int64))
+    seq_start = np.asarray(seq_start, np.int64)
+    check_structure(parent, seq_start)
+    if cache_start is not None:
+        cache_start = np.asarray(cache_start, np.int64)
+        k_cache = np.asarray(k_cache, np.float64)
+        v_cache = np.asarray(v_cache, np.float64)
+        if cache_start.shape != seq_start.shape or cache_start[0] != 0 or np.any(np.diff(cache_start) < 0) \
+                or cache_start[-1] != k_cache.shape[0]:
+            raise ValueError("cache_start is not a CSR over the cached rows, one range per sequence")
+    tok_seq = np.searchsorted(seq_start, np.arange(parent.shape[0]), side="right") - 1
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     if Hq % Hkv:
@@ -69,7 +86,13 @@ def fork_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, parent: np.ndarr
         vis = visible_tokens(parent, int(t))
         for h in range(Hq):
             g = h // G
-            logits = scale * (k[vis, g, :] @ q[t, h, :])
+            keys, vals = k[vis, g, :], v[vis, g, :]
+            if cache_start is not None:
+                s = tok_seq[t]
+                c = slice(cache_start[s], cache_start[s + 1])
+                keys = np.concatenate([k_cache[c, g, :], keys])
+                vals = np.concatenate([v_cache[c, g, :], vals])
+            logits = scale * (keys @ q[t, h, :])
             w = np.exp(logits - logits.max())
-            out[i, h] = (w / w.sum()) @ v[vis, g, :]
+            out[i, h] = (w / w.sum()) @ vals
     return out

@@ -155,3 +155,40 @@ def test_requests_are_isolated_and_structure_checked():
     bad[n + 3] = 2  # a parent in the other request
     with pytest.raises(ValueError):
         fork_attention(q, k, v, bad, np.array([0, n, T]), 0.5)
+
+
+def test_cached_keys_act_as_the_sequence_prefix():
+    """Section 3.4: a request resumed from a checkpoint with cached keys and
+    values computes what the fresh request computes when the cached part is
+    real tokens ahead of it (a chain prefix that every root hangs off)."""
+    rng = np.random.default_rng(8)
+    par, _ = _forest()
+    n = par.shape[0]
+    C, H, D = 23, 2, 8
+    q, k, v = _qkv(rng, n + C, H, H, D)
+    # fresh: C prefix tokens as a chain, the forest's roots hang off the last of them
+    fresh_par = np.concatenate([np.arange(-1, C - 1), np.where(par < 0, C - 1, par + C)])
+    fresh = fork_attention(q, k, v, fresh_par, np.array([0, n + C]), 0.6)
+    # resumed: the prefix only as cached keys and values
+    resumed = fork_attention(q[C:], k[C:], v[C:], par, np.array([0, n]), 0.6, k_cache=k[:C], v_cache=v[:C],
+                             cache_start=np.array([0, C]))
+    assert np.max(np.abs(resumed - fresh[C:])) < 1e-12
+
+
+def test_caches_belong_to_their_sequence():
+    rng = np.random.default_rng(9)
+    par, _ = _forest()
+    n = par.shape[0]
+    T = 2 * n
+    parent = np.concatenate([par, np.where(par < 0, -1, par + n)])
+    q, k, v = _qkv(rng, T, 2, 2, 8)
+    kc, vc = rng.standard_normal((30, 2, 8)), rng.standard_normal((30, 2, 8))
+    both = fork_attention(q, k, v, parent, np.array([0, n, T]), 0.5, k_cache=kc, v_cache=vc,
+                          cache_start=np.array([0, 0, 30]))  # only the second request has cached rows
+    first = fork_attention(q[:n], k[:n], v[:n], par, np.array([0, n]), 0.5)
+    second = fork_attention(q[n:], k[n:], v[n:], par, np.array([0, n]), 0.5, k_cache=kc, v_cache=vc,
+                            cache_start=np.array([0, 30]))
+    assert np.array_equal(both[:n], first) and np.array_equal(both[n:], second)
+    with pytest.raises(ValueError):
+        fork_attention(q, k, v, parent, np.array([0, n, T]), 0.5, k_cache=kc, v_cache=vc,
+                       cache_start=np.array([0, 10, 20]))
