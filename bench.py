@@ -654,9 +654,10 @@ def chain_main(args):
                         "gbs": float(byt.sum() / (per.sum() * 1e-3) / 1e9), "per": per}
         log(f"chain rounds, history capacity {cap}: {per.mean() * 1e3:.1f} us/round, "
             f"{byt.mean() / 1e6:.1f} MB/round, {results[cap]['gbs']:.0f} GB/s")
-    # the bench line: the deferred write (history of 16 tokens); the copy before each step is the
-    # binding keeping this round's keys and gates for the next one
-    d = results[16]
+    # the bench line: the faster of the two modes; the other is reported beside it
+    best = min(results, key=lambda c: results[c]["ms_per_round"])
+    other = 16 if best == 0 else 0
+    d = results[best]
     cpu = parity = None
     if not args.no_cpu_baseline:
         from oracle.chain import chain_rounds
@@ -676,14 +677,14 @@ def chain_main(args):
             "ms_per_step": round(d["ms_per_round"], 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "config": {"workload": f"chain_rounds_{n_seq}x{N}_h{H}_d{D}", "sequences": n_seq, "draft_tokens": N,
-                       "heads": H, "d_k": D, "d_v": D, "history_capacity": 16, "accepted": "uniform 0..4",
+                       "heads": H, "d_k": D, "d_v": D, "history_capacity": best, "accepted": "uniform 0..4",
                        "parallelism": "single GPU"},
             "roofline": {"bound": "hbm", "achieved": round(d["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_chain_step",
                          "launch_unit": "one round", "alg_bytes": d["bytes_per_round"]},
-            "state_every_round": {"ms_per_round": round(results[0]["ms_per_round"], 5),
-                                  "bytes_per_round": results[0]["bytes_per_round"],
-                                  "hbm_frac": round(results[0]["gbs"] / HBM_PEAK_GBS, 4)},
+            "other_mode": {"history_capacity": other, "ms_per_round": round(results[other]["ms_per_round"], 5),
+                           "bytes_per_round": results[other]["bytes_per_round"],
+                           "hbm_frac": round(results[other]["gbs"] / HBM_PEAK_GBS, 4)},
             "cpu_baseline": cpu, "parity_vs_oracle": parity,
             "step_ms_percentiles": {"p10": round(float(np.percentile(d["per"], 10)), 5),
                                     "p50": round(float(np.median(d["per"])), 5),

@@ -104,6 +104,7 @@ typedef enum gdn_dev_error {
   GDN_DEV_NOT_PLANNED = 8,    /* GDN_FWD_PLANNED on a workspace without a matching plan; index = 0 */
   GDN_DEV_CHAIN = 9,          /* gdn_chain_step: an accepted count outside [0, N] or a history length outside
                                  [0, hist_cap]; index = the first such sequence (it is skipped) */
+  GDN_DEV_CACHE = 10,         /* gdn_tree_attention: cache_start is not a CSR over [0, Tc]; index = position */
 } gdn_dev_error;
 
 /*
@@ -326,6 +327,14 @@ typedef struct gdn_attn_dims {
  *  workspace                 at least gdn_tree_attention_workspace_size bytes, 256-byte aligned;
  *                            its error word is read with gdn_tree_check_error
  *  flags                     0 or GDN_ATTN_PLANNED
+ *  k_cache, v_cache [Tc, Hkv, D], cache_start [n_seq + 1], Tc
+ *                            cached keys and values of resumed states (Flide section 3.4: a
+ *                            checkpoint keeps the full-attention keys and values before its
+ *                            position): every token of sequence s also sees cached rows
+ *                            [cache_start[s], cache_start[s + 1]), ahead of its root path.
+ *                            cache_start NULL: no cache. bf16, 16-byte aligned. cache_start is
+ *                            checked on the device (GDN_DEV_CACHE); it may change between calls
+ *                            that reuse one plan.
  */
 typedef struct gdn_attn_args {
   gdn_attn_dims dims;
@@ -339,6 +348,10 @@ typedef struct gdn_attn_args {
   void* workspace;
   size_t workspace_bytes;
   uint32_t flags;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cache_start;
+  int64_t Tc;
 } gdn_attn_args;
 
 /* Workspace bytes of gdn_tree_attention for these sizes. Host only. */
@@ -377,8 +390,10 @@ int gdn_tree_attention(const gdn_attn_args* a, void* stream);
  * v [n_seq, N, H, Dv]; prev_g, log_gate, beta [n_seq, N, H]; accepted,
  * hist_len_in, hist_len_out [n_seq] int32. Sizes: N in [1, 32], Dk in {32, 64,
  * 128}, Dv a multiple of 16 up to 128, hist_cap >= 0 (0: the state is written
- * every round). workspace: at least gdn_tree_commit_workspace_size() bytes; its
- * error word (GDN_DEV_CHAIN) is read with gdn_tree_check_error.
+ * every round). ckpt, state_out, hist_pv, hist_k, prev_pv, prev_k, q, k and v
+ * must be 16-byte aligned (they are moved in 16-byte pieces). workspace: at
+ * least gdn_tree_commit_workspace_size() bytes; its error word (GDN_DEV_CHAIN)
+ * is read with gdn_tree_check_error.
  */
 #define GDN_CHAIN_FLUSH 1u
 

@@ -168,3 +168,53 @@ def test_level_capacity_is_reported():
         B.attention(f(q), f(k), f(v), parent, seq, max_levels=2, out=out, check=True)
     assert ei.value.code == 5
     assert bool((out == 3.0).all())  # nothing computed
+
+
+def test_cached_keys_resume_a_request():
+    """Flide section 3.4: a request resumed with cached keys and values of its
+    checkpoint matches the fresh request (the cached part as real prefix
+    tokens) and the oracle; sequences without cached rows and draft trees over
+    cached rows share the stream; a bad cache_start is refused on the device."""
+    from tree_forked_gated_amd import binding as B
+    rng = np.random.default_rng(16)
+    Hq, Hkv = 4, 2
+    pa, sa = _stream([150], forks=[(0, 100, 40), (0, 149, 20)])
+    pb, sb = _stream([70], drafts=[30])  # a chain and a draft tree
+    na, nb = pa.shape[0], pb.shape[0]
+    C0, C2 = 131, 40  # cached rows of sequences 0 and 2 (sequence 1 has none)
+    parent = np.concatenate([pa, np.where(pb < 0, -1, pb + na)]).astype(np.int32)
+    seq = np.concatenate([sa, sb[1:] + na]).astype(np.int32)
+    T = na + nb
+    q, k, v = _values(rng, T, Hq, Hkv)
+    _, kc, vc = _values(rng, C0 + C2, Hq, Hkv)
+    cache_start = np.array([0, C0, C0, C0 + C2], np.int32)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(torch.bfloat16)
+    lv = _levels(parent, seq)
+    out, ws = B.attention(f(q), f(k), f(v), parent, seq, scale=0.125, max_levels=lv, k_cache=f(kc), v_cache=f(vc),
+                          cache_start=cache_start, check=True)
+    torch.cuda.synchronize()
+    ref = fork_attention(q, k, v, parent, seq, 0.125, k_cache=kc, v_cache=vc, cache_start=cache_start)
+    say(f"attention with cached keys: T={T}, cached rows {C0} + {C2}")
+    _compare("cached_keys", out.float().cpu().numpy(), ref)
+    # the fresh request: sequence 0's cached rows as a chain prefix that its roots hang off
+    fp = np.concatenate([np.arange(-1, C0 - 1), np.where(pa < 0, C0 - 1, pa + C0)]).astype(np.int32)
+    fresh, _ = B.attention(f(np.concatenate([np.zeros((C0, Hq, 128), np.float32), q[:na]])),
+                           f(np.concatenate([kc[:C0], k[:na]])), f(np.concatenate([vc[:C0], v[:na]])), fp,
+                           np.array([0, C0 + na], np.int32), scale=0.125, max_levels=_levels(fp, [0, C0 + na]),
+                           check=True)
+    torch.cuda.synchronize()
+    e = rel_l2(out[:na].float().cpu().numpy(), fresh[C0:].float().cpu().numpy().astype(np.float64))
+    say(f"  resumed vs fresh request: rel-L2 {e:.3e}")
+    assert e <= 1e-2
+    # a planned workspace serves another cache for the same stream; a bad cache_start is refused
+    cs2 = np.array([0, 5, 5, 45], np.int32)
+    out2, _ = B.attention(f(q), f(k), f(v), parent, seq, scale=0.125, max_levels=lv, workspace=ws, planned=True,
+                          k_cache=f(kc[:45]), v_cache=f(vc[:45]), cache_start=cs2, check=True)
+    torch.cuda.synchronize()
+    ref2 = fork_attention(q, k, v, parent, seq, 0.125, k_cache=kc[:45], v_cache=vc[:45], cache_start=cs2)
+    _compare("cached_keys_replanned", out2.float().cpu().numpy(), ref2)
+    with pytest.raises(B.GdnDeviceError) as ei:
+        B.attention(f(q), f(k), f(v), parent, seq, scale=0.125, max_levels=lv, workspace=ws, planned=True,
+                    k_cache=f(kc[:45]), v_cache=f(vc[:45]), cache_start=np.array([0, 30, 20, 45], np.int32),
+                    check=True)
+    assert ei.value.code == 10 and ei.value.index == 2

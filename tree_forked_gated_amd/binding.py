@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libgdn_tree.so")
 GDN_F32, GDN_BF16 = 0, 1
 DEV_ERRORS = {0: "ok", 1: "seq_start", 2: "parent order", 3: "parent in another sequence", 4: "fork capacity",
               5: "level capacity", 6: "rows", 7: "commit path", 8: "workspace not planned for these sizes",
-              9: "accepted count or history length out of range"}
+              9: "accepted count or history length out of range", 10: "cache_start"}
 CHUNK = 64
 FWD_PLANNED = 1  # gdn_tree.h GDN_FWD_PLANNED: reuse the metadata already in the workspace
 
@@ -59,7 +59,8 @@ class AttnArgs(ctypes.Structure):
     _fields_ = [("dims", AttnDims), ("scale", ctypes.c_float), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("parent_idx", ctypes.c_void_p), ("seq_start", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("cache_start", ctypes.c_void_p), ("Tc", ctypes.c_int64)]
 
 
 ATTN_PLANNED = 1  # gdn_tree.h GDN_ATTN_PLANNED
@@ -378,10 +379,12 @@ def attention_workspace_size(dims: AttnDims) -> int:
 
 
 def attention(q, k, v, parent_idx, seq_start, *, max_levels, scale=None, workspace=None, out=None, planned=False,
-              stream=None, check=False):
+              stream=None, check=False, k_cache=None, v_cache=None, cache_start=None):
     """gdn_tree_attention (ForkAttention) on device tensors: q [T,Hq,D], k and
     v [T,Hkv,D] bf16; returns (out [T,Hq,D], workspace). max_levels is the
-    fork-nesting capacity (as for forward); scale defaults to 1/sqrt(D)."""
+    fork-nesting capacity (as for forward); scale defaults to 1/sqrt(D).
+    k_cache, v_cache [Tc,Hkv,D] and cache_start [n_seq+1]: cached keys and
+    values each sequence sees ahead of its tokens (optional)."""
     device = q.device
     T, Hq, D = q.shape
     Hkv = k.shape[1]
@@ -401,6 +404,12 @@ def attention(q, k, v, parent_idx, seq_start, *, max_levels, scale=None, workspa
     a.workspace = _ptr(workspace)
     a.workspace_bytes = int(workspace.numel())
     a.flags = ATTN_PLANNED if planned else 0
+    if cache_start is not None:
+        cache_start = _i32(cache_start, device)
+        a.cache_start = _ptr(cache_start)
+        a.Tc = int(k_cache.shape[0])
+        if a.Tc > 0:
+            a.k_cache, a.v_cache = _ptr(k_cache), _ptr(v_cache)
     _check(lib.gdn_tree_attention(ctypes.byref(a), _stream(stream)), "gdn_tree_attention")
     if check:
         raise_device_error(workspace, stream)

@@ -218,6 +218,7 @@ const char* gdn_tree_strerror(int code) {
     case 100 + GDN_DEV_PATH: return "a commit path is not a root-to-node parent chain";
     case 100 + GDN_DEV_NOT_PLANNED: return "GDN_FWD_PLANNED on a workspace without a matching plan";
     case 100 + GDN_DEV_CHAIN: return "an accepted count or history length is out of range";
+    case 100 + GDN_DEV_CACHE: return "cache_start is not a CSR over [0, Tc]";
     default: return "unknown code";
   }
 }
@@ -354,6 +355,12 @@ int gdn_tree_attention(const gdn_attn_args* a, void* stream) {
     return fail(GDN_ERR_ARGS, "q, k, v and out must be 16-byte aligned");
   if (((uintptr_t)a->workspace & 255u) != 0) return fail(GDN_ERR_ARGS, "workspace must be 256-byte aligned");
   if (a->flags & ~GDN_ATTN_PLANNED) return fail(GDN_ERR_ARGS, "unknown flags");
+  if (a->cache_start) {
+    if (a->Tc < 0 || a->Tc > 0x7fffffffLL) return fail(GDN_ERR_DIMS, "Tc must be in [0, 2^31)");
+    if (a->Tc > 0 && (!a->k_cache || !a->v_cache)) return fail(GDN_ERR_NULL, "k_cache and v_cache are required");
+    if (!aligned16(a->k_cache) || !aligned16(a->v_cache))
+      return fail(GDN_ERR_ARGS, "k_cache and v_cache must be 16-byte aligned");
+  }
   if (!(a->scale > 0.f) || a->scale > 3.0e38f) return fail(GDN_ERR_ARGS, "scale must be positive and finite");
   AttnLayout A;
   if (!attn_layout(d, &A)) return fail(GDN_ERR_DIMS, "bad sizes");
@@ -381,8 +388,9 @@ int gdn_chain_step(const gdn_chain_args* a, void* stream) {
       return fail(GDN_ERR_NULL, "hist_pv, hist_k and hist_g are required when hist_cap > 0");
     if ((const void*)a->hist_len_in == (const void*)a->hist_len_out || (const void*)a->prev_pv == (const void*)a->pseudo_v)
       return fail(GDN_ERR_ARGS, "hist_len_out and pseudo_v must be other buffers than hist_len_in and prev_pv");
-    if (!aligned16(a->ckpt) || !aligned16(a->state_out))
-      return fail(GDN_ERR_ARGS, "ckpt and state_out must be 16-byte aligned");
+    if (!aligned16(a->ckpt) || !aligned16(a->state_out) || !aligned16(a->hist_pv) || !aligned16(a->hist_k) ||
+        !aligned16(a->prev_pv) || !aligned16(a->prev_k) || !aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v))
+      return fail(GDN_ERR_ARGS, "ckpt, state_out, hist_pv, hist_k, prev_pv, prev_k, q, k and v must be 16-byte aligned");
     if (a->workspace_bytes < 8) return fail(GDN_ERR_WORKSPACE, "the chain workspace holds an 8-byte error word");
   }
   if (a->flags & ~GDN_CHAIN_FLUSH) return fail(GDN_ERR_ARGS, "unknown flags");

@@ -44,7 +44,8 @@ constexpr int D = 128;        // head dimension
 constexpr int kT = 64;        // keys per tile, queries per chunk
 constexpr int kThr = 256;     // four waves
 constexpr int kTileB = kT * D * 2;  // bytes of one K or V tile (bf16)
-constexpr int kMaxSpans = 64;  // span capacity per item (fork nesting levels)
+constexpr int kMaxLevels = 64;  // fork nesting levels an item's span list may hold
+constexpr int kMaxSpans = kMaxLevels + 1;  // plus the sequence's cached keys
 constexpr int oK = 0;                   // [2] K tiles
 constexpr int oV = 2 * kTileB;          // [2] V tiles
 constexpr int oSp = 4 * kTileB;         // the item's spans (int2)
@@ -62,6 +63,9 @@ struct AttnArgs {
   const int2* spans;      // [item][max_levels] inclusive key spans; span 0 is the item's own segment
   const int* n_items;
   int* claim;
+  const __bf16* k_cache;
+  const __bf16* v_cache;
+  const int* cache_start;  // null: no cached keys
   int Hq, Hkv, max_levels;
   float c;  // scale * log2(e), positive
 };
@@ -76,6 +80,11 @@ __device__ __forceinline__ uint32_t lds_addr_of(const unsigned char* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((const lds_void*)p));
 }
 __device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// A wave-uniform pointer made explicit (the copies take their base address in scalar registers).
+__device__ __forceinline__ const __bf16* rfl_ptr(const __bf16* p) {
+  const unsigned long long u = (unsigned long long)p;
+  return (const __bf16*)(((unsigned long long)(unsigned)rfl((int)(u >> 32)) << 32) | (unsigned)rfl((int)u));
+}
 // 16-byte piece p of tile row r sits at slot p ^ swz(r) (spreads the rows over the LDS banks)
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ i16x4 tr_read(const unsigned char* p) {
@@ -102,7 +111,8 @@ __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) { return __b
 __device__ __forceinline__ void issue_tile(const __bf16* head0, int row0, int n, unsigned rs, unsigned char* tile,
                                            int w, int lane) {
   const int g4 = lane >> 4, l16 = lane & 15;
-  const unsigned char* src = reinterpret_cast<const unsigned char*>(head0) + (size_t)row0 * rs + (size_t)(16 * w) * rs;
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(rfl_ptr(head0)) + (size_t)rfl(row0) * rs +
+                             (size_t)(16 * w) * rs;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int blk = 4 * w + b;
@@ -119,18 +129,19 @@ struct Tile {
   int sp;                  // span index
 };
 
-// The tile after (sp, k0) in the item's span list (spans in LDS).
-__device__ __forceinline__ Tile next_tile(const int2* sps, int nsp, int sp, int k0, int q0, int tree) {
+// The tile after (sp, k0) in the item's span list (spans in LDS; span `own` is
+// the item's own segment, a span before it the cached keys).
+__device__ __forceinline__ Tile next_tile(const int2* sps, int nsp, int own, int sp, int k0, int q0, int tree) {
   Tile t = {0, 0, 0, 0, 0};
   while (sp < nsp) {
     const int2 s = sps[sp];
     if (k0 < 0) k0 = s.x;
-    if (k0 <= s.y) {
+    if (k0 <= s.y) {  // every field wave-uniform (the spans are the same for every lane)
       t.valid = 1;
-      t.sp = sp;
-      t.k0 = k0;
-      t.n = min(kT, s.y - k0 + 1);
-      t.kind = (sp == 0 && k0 == q0) ? (tree ? 2 : 1) : 0;
+      t.sp = rfl(sp);
+      t.k0 = rfl(k0);
+      t.n = rfl(min(kT, s.y - k0 + 1));
+      t.kind = rfl((sp == own && k0 == q0) ? (tree ? 2 : 1) : 0);
       return t;
     }
     ++sp;
@@ -141,7 +152,7 @@ __device__ __forceinline__ Tile next_tile(const int2* sps, int nsp, int sp, int 
 
 // HPW query heads of one key/value group per wave: every K and V fragment read
 // from LDS feeds HPW matrix products.
-template <int HPW>
+template <int HPW, bool CACHE>
 __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_claim;
@@ -179,8 +190,15 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
     const int hk = h0 / G;
     const int4 inf = a.item_info[item];
     const int q0 = rfl(inf.x), nq = rfl(inf.y), tree = rfl(inf.z & 1), sq = rfl(inf.z >> 1);
-    const int nsp = rfl(min(inf.w, kMaxSpans));
-    if (tid < nsp) sps[tid] = a.spans[(size_t)item * a.max_levels + tid];
+    // the sequence's cached keys, if any, come first (span 0), then the item's spans
+    int own = 0;
+    if (CACHE) {
+      const int c0 = a.cache_start[sq], c1 = a.cache_start[sq + 1];
+      own = rfl(c1 > c0 ? 1 : 0);
+      if (own && tid == 0) sps[0] = make_int2(c0, c1 - 1);
+    }
+    const int nsp = rfl(min(inf.w, kMaxLevels)) + own;
+    if (tid >= own && tid < nsp) sps[tid] = a.spans[(size_t)item * a.max_levels + tid - own];
     // this wave's 16 queries of each head as MFMA fragments (zero past the chunk's queries)
     const int qi = 16 * w + l16;  // query within the chunk
     bf16x8 Qf[HPW][4];
@@ -201,11 +219,14 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
     }
     const __bf16* k0p = a.k + (size_t)hk * D;
     const __bf16* v0p = a.v + (size_t)hk * D;
+    const __bf16* kc0p = CACHE ? a.k_cache + (size_t)hk * D : k0p;
+    const __bf16* vc0p = CACHE ? a.v_cache + (size_t)hk * D : v0p;
     __syncthreads();  // spans in LDS
-    Tile cur = next_tile(sps, nsp, 0, -1, q0, tree);
+    Tile cur = next_tile(sps, nsp, own, 0, -1, q0, tree);
     if (cur.valid) {
-      issue_tile(k0p, cur.k0, cur.n, rs_kv, smem + oK, w, lane);
-      issue_tile(v0p, cur.k0, cur.n, rs_kv, smem + oV, w, lane);
+      const bool cc = cur.sp < own;
+      issue_tile(cc ? kc0p : k0p, cur.k0, cur.n, rs_kv, smem + oK, w, lane);
+      issue_tile(cc ? vc0p : v0p, cur.k0, cur.n, rs_kv, smem + oV, w, lane);
     }
     wait_vm();
     lds_barrier();
@@ -220,11 +241,12 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
     }
     const bool active = 16 * w < nq;
     for (int it = 0; cur.valid; ++it) {
-      const Tile nxt = next_tile(sps, nsp, cur.sp, cur.k0 + kT, q0, tree);
+      const Tile nxt = next_tile(sps, nsp, own, cur.sp, cur.k0 + kT, q0, tree);
       const int b = it & 1;
       if (nxt.valid) {
-        issue_tile(k0p, nxt.k0, nxt.n, rs_kv, smem + oK + (b ^ 1) * kTileB, w, lane);
-        issue_tile(v0p, nxt.k0, nxt.n, rs_kv, smem + oV + (b ^ 1) * kTileB, w, lane);
+        const bool cc = nxt.sp < own;
+        issue_tile(cc ? kc0p : k0p, nxt.k0, nxt.n, rs_kv, smem + oK + (b ^ 1) * kTileB, w, lane);
+        issue_tile(cc ? vc0p : v0p, nxt.k0, nxt.n, rs_kv, smem + oV + (b ^ 1) * kTileB, w, lane);
       }
       if (active) {
         const unsigned char* kt = smem + oK + b * kTileB;
@@ -374,9 +396,22 @@ __device__ inline int seg_containing(const int* seg_start, int n_seg, int t) {
 
 // One workgroup: chunk items of every segment (in stream order) and each
 // item's key spans: its own segment's prefix, then the ancestor segments' prefixes.
-__global__ void __launch_bounds__(1024) k_attn_items(Meta m, ItemTables t, int max_levels) {
+// cache_start must be a CSR over [0, Tc]: a bad entry raises GDN_DEV_CACHE (the
+// attention kernel then computes nothing, so no cached row outside [0, Tc) is read).
+__device__ inline void check_cache(const Meta& m, const int* cache_start, int n_seq, long long Tc) {
+  if (!cache_start) return;
+  for (int s = threadIdx.x; s <= n_seq; s += blockDim.x) {
+    const int v = cache_start[s];
+    const bool bad = (s == 0 && v != 0) || (s > 0 && (v < cache_start[s - 1] || v > Tc)) || (s == n_seq && v != Tc);
+    if (bad) raise_error(m.err, GDN_DEV_CACHE, s);
+  }
+}
+
+__global__ void __launch_bounds__(1024) k_attn_items(Meta m, ItemTables t, int max_levels, const int* cache_start,
+                                                     int n_seq, long long Tc) {
   __shared__ int sh[17];
   const int tid = threadIdx.x;
+  check_cache(m, cache_start, n_seq, Tc);
   const int n_seg = (*m.err != kNoError) ? 0 : *m.n_seg;
   int run = 0;
   for (int base = 0; base < n_seg; base += 1024) {
@@ -413,11 +448,13 @@ __global__ void __launch_bounds__(1024) k_attn_items(Meta m, ItemTables t, int m
   }
 }
 
-__global__ void k_attn_replan(Meta m, int* claim, unsigned long long tag) {
+__global__ void k_attn_replan(Meta m, int* claim, unsigned long long tag, const int* cache_start, int n_seq,
+                              long long Tc) {
   if (threadIdx.x == 0) {
     *claim = 0;
     if (*m.plan_tag != tag) raise_error(m.err, GDN_DEV_NOT_PLANNED, 0);
   }
+  check_cache(m, cache_start, n_seq, Tc);
 }
 
 }  // namespace
@@ -464,11 +501,13 @@ hipError_t launch_attention(const gdn_attn_args& aa, const AttnLayout& A, hipStr
   const unsigned long long tag = plan_fingerprint(pa);
   hipError_t e;
   if (aa.flags & GDN_ATTN_PLANNED) {
-    hipLaunchKernelGGL(k_attn_replan, dim3(1), dim3(64), 0, s, m, t.claim, tag);
+    hipLaunchKernelGGL(k_attn_replan, dim3(1), dim3(256), 0, s, m, t.claim, tag, aa.cache_start, aa.dims.n_seq,
+                       (long long)aa.Tc);
   } else {
     e = launch_plan(pa, m, A.plan, tag, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_items, dim3(1), dim3(1024), 0, s, m, t, aa.dims.max_levels);
+    hipLaunchKernelGGL(k_attn_items, dim3(1), dim3(1024), 0, s, m, t, aa.dims.max_levels, aa.cache_start,
+                       aa.dims.n_seq, (long long)aa.Tc);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -484,23 +523,26 @@ hipError_t launch_attention(const gdn_attn_args& aa, const AttnLayout& A, hipStr
   x.spans = t.spans;
   x.n_items = t.n_items;
   x.claim = t.claim;
+  x.k_cache = reinterpret_cast<const __bf16*>(aa.k_cache);
+  x.v_cache = reinterpret_cast<const __bf16*>(aa.v_cache);
+  x.cache_start = aa.cache_start;
   x.Hq = aa.dims.Hq;
   x.Hkv = aa.dims.Hkv;
   x.max_levels = aa.dims.max_levels;
   x.c = aa.scale * kLog2e;
-  // two query heads per wave when a key/value group has an even number of them
-  const bool two = (aa.dims.Hq / aa.dims.Hkv) % 2 == 0;
-  const void* kern = two ? reinterpret_cast<const void*>(k_fork_attn<2>) : reinterpret_cast<const void*>(k_fork_attn<1>);
+  // two query heads per wave when a key/value group has an even number of them; cached keys in a variant of their own
+  const bool two = (aa.dims.Hq / aa.dims.Hkv) % 2 == 0, cache = aa.cache_start != nullptr;
+  void (*kern)(const AttnArgs) = two ? (cache ? k_fork_attn<2, true> : k_fork_attn<2, false>)
+                                     : (cache ? k_fork_attn<1, true> : k_fork_attn<1, false>);
   int cus = 0, occ = 1;
-  e = ensure_dynamic_lds(kern, kLds, kThr, &occ);
+  e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), kLds, kThr, &occ);
   if (e != hipSuccess) return e;
   e = current_device_cus(&cus);
   if (e != hipSuccess) return e;
-  if (two) hipLaunchKernelGGL(k_fork_attn<2>, dim3(cus * occ), dim3(kThr), kLds, s, x);
-  else hipLaunchKernelGGL(k_fork_attn<1>, dim3(cus * occ), dim3(kThr), kLds, s, x);
+  hipLaunchKernelGGL(kern, dim3(cus * occ), dim3(kThr), kLds, s, x);
   return hipGetLastError();
 }
 
-int attn_max_spans() { return kMaxSpans; }
+int attn_max_spans() { return kMaxLevels; }
 
 }  // namespace gdn

@@ -18,7 +18,8 @@
 //   vt_t = beta_t (v_t - alpha_t S k_t),  S <- alpha_t S + vt_t k_t^T,  o_t = S q_t.
 //
 // One workgroup per (sequence, head, 32 rows of S); a thread holds 16 (d_k /
-// 8) consecutive columns of one row. Every launch shape depends only on the
+// 8) columns of one row, in four groups of four (each 16-byte access of a row's
+// eight threads covers 128 contiguous bytes). Every launch shape depends only on the
 // sizes; the accepted counts and history lengths are device data.
 #include "gdn_internal.h"
 
@@ -27,7 +28,7 @@ namespace {
 
 constexpr int kRows = 32;   // rows of S (d_v) per workgroup
 constexpr int kThr = 256;   // 8 threads per row
-constexpr int kTileP = 16;  // path tokens staged in LDS at a time
+constexpr int kTileP = 32;  // path tokens staged in LDS at a time
 
 struct ChainArgs {
   float* ckpt;
@@ -71,14 +72,70 @@ __device__ void check_all(const ChainArgs& a) {
                                  : (((unsigned long long)(unsigned)GDN_DEV_CHAIN << 32) | (unsigned)s_bad);
 }
 
+// 16-byte vector of E as floats.
+template <typename E>
+struct Vec16;
+template <>
+struct Vec16<float> {
+  static constexpr int n = 4;
+  __device__ static void load(const float* p, float* dst) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    dst[0] = x.x, dst[1] = x.y, dst[2] = x.z, dst[3] = x.w;
+  }
+};
+template <>
+struct Vec16<__bf16> {
+  static constexpr int n = 8;
+  __device__ static void load(const __bf16* p, float* dst) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    const unsigned w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dst[2 * i] = __uint_as_float(w[i] << 16);
+      dst[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+// Path tokens [j0, j0 + nt) of the commit: history slots below hl, then tokens of
+// the previous draft. Keys and pseudo-value rows are read in 16-byte pieces.
+template <typename E, int DK>
+__device__ inline void stage_path(const ChainArgs& a, int s, int h, int v0, int rows, int hl, int j0, int nt,
+                                  float (*sK)[DK + 4], float (*sV)[kRows], float* sG) {
+  constexpr int VE = Vec16<E>::n;
+  const int tid = threadIdx.x, H = a.H, N = a.N, Dv = a.Dv;
+  const E* pk = reinterpret_cast<const E*>(a.prev_k);
+  const E* pg = reinterpret_cast<const E*>(a.prev_g);
+  const E* hk = reinterpret_cast<const E*>(a.hist_k);
+  for (int idx = tid; idx < nt * (DK / VE); idx += kThr) {
+    const int jj = idx / (DK / VE), part = idx % (DK / VE), j = j0 + jj;
+    const E* src = j < hl ? hk + (((size_t)s * a.cap + j) * H + h) * DK : pk + (((size_t)s * N + (j - hl)) * H + h) * DK;
+    Vec16<E>::load(src + part * VE, &sK[jj][part * VE]);
+  }
+  for (int idx = tid; idx < nt * (kRows / 4); idx += kThr) {
+    const int jj = idx / (kRows / 4), c4 = idx % (kRows / 4), j = j0 + jj;
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (4 * c4 < rows) {
+      const float* src = j < hl ? a.hist_pv + (((size_t)s * a.cap + j) * H + h) * Dv
+                                : a.prev_pv + (((size_t)s * N + (j - hl)) * H + h) * Dv;
+      x = *reinterpret_cast<const float4*>(src + v0 + 4 * c4);
+    }
+    *reinterpret_cast<float4*>(&sV[jj][4 * c4]) = x;
+  }
+  if (tid < nt) {
+    const int j = j0 + tid;
+    sG[tid] = j < hl ? a.hist_g[((size_t)s * a.cap + j) * H + h] : upc<E>(pg[((size_t)s * N + (j - hl)) * H + h]);
+  }
+}
+
 template <typename E, int DK>
 __global__ void __launch_bounds__(kThr) k_chain_step(const ChainArgs a) {
   constexpr int CPT = DK / 8;  // columns per thread
+  constexpr int VE = Vec16<E>::n;
   __shared__ float sK[kTileP][DK + 4];
   __shared__ float sV[kTileP][kRows];
   __shared__ float sG[kTileP];
   __shared__ float sW[kTileP];
-  __shared__ float sSigma;
   extern __shared__ float dyn[];  // draft: k [N][DK], q [N][DK], v [N][kRows], gate [N], beta [N]
   const int s = blockIdx.x, h = blockIdx.y, vb = blockIdx.z;
   const int tid = threadIdx.x, r = tid >> 3, cq = tid & 7;
@@ -90,132 +147,137 @@ __global__ void __launch_bounds__(kThr) k_chain_step(const ChainArgs a) {
   const int acc = a.accepted[s], hl = a.hist_len_in[s];
   if (acc < 0 || acc > N || hl < 0 || hl > a.cap) return;  // reported by check_all
   const size_t SS = (size_t)Dv * DK;
-  const E* pk = reinterpret_cast<const E*>(a.prev_k);
-  const E* pg = reinterpret_cast<const E*>(a.prev_g);
   E* hk = reinterpret_cast<E*>(a.hist_k);
 
-  // the checkpoint rows
+  // every independent load first: the checkpoint rows, the draft, the path's last tile.
+  // Element 4 i4 + e of a thread is column 4 cq + 32 i4 + e of its row, so that
+  // the eight threads of a row read 128 contiguous bytes per instruction.
   float S[CPT];
-  const float* ck = a.ckpt + ((size_t)s * H + h) * SS + (size_t)(v0 + r) * DK + cq * CPT;
+  const float* ck = a.ckpt + ((size_t)s * H + h) * SS + (size_t)(v0 + r) * DK + 4 * cq;
 #pragma unroll
   for (int i = 0; i < CPT; i += 4) {
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row_ok) x = *reinterpret_cast<const float4*>(ck + i);
+    if (row_ok) x = *reinterpret_cast<const float4*>(ck + 8 * i);
     S[i] = x.x;
     S[i + 1] = x.y;
     S[i + 2] = x.z;
     S[i + 3] = x.w;
   }
-
-  // commit (Eq. 3) over the path: history slots [0, hl), then draft tokens [0, acc)
-  const int L = hl + acc;
-  float accum[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) accum[i] = 0.f;
-  if (tid == 0) sSigma = 0.f;
-  __syncthreads();
-  for (int tile_end = L; tile_end > 0; tile_end -= kTileP) {
-    const int tile_beg = max(0, tile_end - kTileP);
-    const int nt = tile_end - tile_beg;
-    if (tid < nt) {
-      const int j = tile_beg + tid;
-      sG[tid] = j < hl ? a.hist_g[((size_t)s * a.cap + j) * H + h]
-                       : upc<E>(pg[((size_t)s * N + (j - hl)) * H + h]);
-    }
-    for (int idx = tid; idx < nt * DK; idx += kThr) {
-      const int jj = idx / DK, d = idx % DK, j = tile_beg + jj;
-      sK[jj][d] = j < hl ? upc<E>(hk[(((size_t)s * a.cap + j) * H + h) * DK + d])
-                         : upc<E>(pk[(((size_t)s * N + (j - hl)) * H + h) * DK + d]);
-    }
-    for (int idx = tid; idx < nt * kRows; idx += kThr) {
-      const int jj = idx / kRows, rr = idx % kRows, j = tile_beg + jj;
-      float x = 0.f;
-      if (rr < rows)
-        x = j < hl ? a.hist_pv[(((size_t)s * a.cap + j) * H + h) * Dv + v0 + rr]
-                   : a.prev_pv[(((size_t)s * N + (j - hl)) * H + h) * Dv + v0 + rr];
-      sV[jj][rr] = x;
-    }
-    __syncthreads();
-    if (tid == 0) {  // exp(sum of the log gates after token j), accumulated from the path's end
-      float sigma = sSigma;
-      for (int jj = nt - 1; jj >= 0; --jj) {
-        sW[jj] = __expf(sigma);
-        sigma += sG[jj];
-      }
-      sSigma = sigma;
-    }
-    __syncthreads();
-    for (int jj = nt - 1; jj >= 0; --jj) {
-      const float wv = sW[jj] * sV[jj][r];
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) accum[i] += wv * sK[jj][cq * CPT + i];
-    }
-    __syncthreads();
-  }
-  const float gall = __expf(sSigma);
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) S[i] = gall * S[i] + accum[i];
-
-  // flush the committed state, or keep the accepted tokens as history
-  const bool flush = a.flush || L > a.cap;
-  float* stores[2] = {flush ? a.ckpt : nullptr, a.state_out};
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    if (!stores[w] || !row_ok) continue;
-    float* dst = stores[w] + ((size_t)s * H + h) * SS + (size_t)(v0 + r) * DK + cq * CPT;
-#pragma unroll
-    for (int i = 0; i < CPT; i += 4) *reinterpret_cast<float4*>(dst + i) = make_float4(S[i], S[i + 1], S[i + 2], S[i + 3]);
-  }
-  if (!flush) {
-    for (int idx = tid; idx < acc * kRows; idx += kThr) {
-      const int i = idx / kRows, rr = idx % kRows;
-      if (rr < rows)
-        a.hist_pv[(((size_t)s * a.cap + hl + i) * H + h) * Dv + v0 + rr] =
-            a.prev_pv[(((size_t)s * N + i) * H + h) * Dv + v0 + rr];
-    }
-    if (vb == 0) {
-      for (int idx = tid; idx < acc * DK; idx += kThr) {
-        const int i = idx / DK, d = idx % DK;
-        hk[(((size_t)s * a.cap + hl + i) * H + h) * DK + d] = pk[(((size_t)s * N + i) * H + h) * DK + d];
-      }
-      if (tid < acc) a.hist_g[((size_t)s * a.cap + hl + tid) * H + h] = upc<E>(pg[((size_t)s * N + tid) * H + h]);
-    }
-  }
-  if (h == 0 && vb == 0 && tid == 0) a.hist_len_out[s] = flush ? 0 : L;
-
-  // verify the new draft from S
   float* dK = dyn;
   float* dQ = dK + (size_t)N * DK;
   float* dV = dQ + (size_t)N * DK;
   float* dG = dV + (size_t)N * kRows;
   float* dB = dG + N;
-  const E* qg = reinterpret_cast<const E*>(a.q);
-  const E* kg = reinterpret_cast<const E*>(a.k);
-  const E* vg = reinterpret_cast<const E*>(a.v);
-  const E* gg = reinterpret_cast<const E*>(a.g);
-  const E* bg = reinterpret_cast<const E*>(a.b);
-  for (int idx = tid; idx < N * DK; idx += kThr) {
-    const int t = idx / DK, d = idx % DK;
-    const size_t o = (((size_t)s * N + t) * H + h) * DK + d;
-    dK[idx] = upc<E>(kg[o]);
-    dQ[idx] = upc<E>(qg[o]);
+  {
+    const E* qg = reinterpret_cast<const E*>(a.q);
+    const E* kg = reinterpret_cast<const E*>(a.k);
+    const E* vg = reinterpret_cast<const E*>(a.v);
+    const E* gg = reinterpret_cast<const E*>(a.g);
+    const E* bg = reinterpret_cast<const E*>(a.b);
+    for (int idx = tid; idx < 2 * N * (DK / VE); idx += kThr) {
+      const int which = idx / (N * (DK / VE)), rem = idx % (N * (DK / VE));
+      const int t = rem / (DK / VE), part = rem % (DK / VE);
+      const size_t o = (((size_t)s * N + t) * H + h) * DK + part * VE;
+      Vec16<E>::load((which ? qg : kg) + o, (which ? dQ : dK) + (size_t)t * DK + part * VE);
+    }
+    constexpr int VPR = kRows / VE;  // 16-byte pieces of a 32-column value row
+    for (int idx = tid; idx < N * VPR; idx += kThr) {
+      const int t = idx / VPR, part = idx % VPR;
+      float* dst = dV + (size_t)t * kRows + part * VE;
+      if (part * VE < rows) Vec16<E>::load(vg + (((size_t)s * N + t) * H + h) * Dv + v0 + part * VE, dst);
+      else
+        for (int i = 0; i < VE; ++i) dst[i] = 0.f;
+    }
+    for (int t = tid; t < N; t += kThr) {
+      dG[t] = upc<E>(gg[((size_t)s * N + t) * H + h]);
+      dB[t] = upc<E>(bg[((size_t)s * N + t) * H + h]);
+    }
   }
-  for (int idx = tid; idx < N * kRows; idx += kThr) {
-    const int t = idx / kRows, rr = idx % kRows;
-    dV[idx] = rr < rows ? upc<E>(vg[(((size_t)s * N + t) * H + h) * Dv + v0 + rr]) : 0.f;
-  }
-  for (int t = tid; t < N; t += kThr) {
-    dG[t] = upc<E>(gg[((size_t)s * N + t) * H + h]);
-    dB[t] = upc<E>(bg[((size_t)s * N + t) * H + h]);
-  }
+  // commit (Eq. 3) over the path: history slots [0, hl), then draft tokens [0, acc),
+  // tiles of 16 tokens from the path's end
+  const int L = hl + acc;
+  int tile_end = L;
+  int nt = min(kTileP, tile_end);
+  if (nt > 0) stage_path<E, DK>(a, s, h, v0, rows, hl, tile_end - nt, nt, sK, sV, sG);
   __syncthreads();
+  float accum[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) accum[i] = 0.f;
+  // the accepted tokens join the history (unless this round flushes), copied from the
+  // staged tile: they are its last acc tokens (acc <= N <= 32 = kTileP)
+  static_assert(kTileP >= 32, "the accepted prefix of a draft must fit one staged tile");
+  const bool flush = a.flush || L > a.cap;
+  if (!flush) {
+    const int j0 = L - nt;  // first path token of the staged tile
+    for (int idx = tid; idx < acc * (kRows / 4); idx += kThr) {
+      const int i = idx / (kRows / 4), c4 = idx % (kRows / 4);
+      if (4 * c4 < rows)
+        *reinterpret_cast<float4*>(a.hist_pv + (((size_t)s * a.cap + hl + i) * H + h) * Dv + v0 + 4 * c4) =
+            *reinterpret_cast<const float4*>(&sV[hl + i - j0][4 * c4]);
+    }
+    if (vb == 0) {
+      for (int idx = tid; idx < acc * DK; idx += kThr) {
+        const int i = idx / DK, d = idx % DK;
+        hk[(((size_t)s * a.cap + hl + i) * H + h) * DK + d] = (E)sK[hl + i - j0][d];
+      }
+      if (tid < acc) a.hist_g[((size_t)s * a.cap + hl + tid) * H + h] = sG[hl + tid - j0];
+    }
+  }
+  float carry = 0.f;  // sum of the log gates after the current tile
+  while (nt > 0) {
+    // weight of token jj: exp(sum of the log gates after it on the path), by a
+    // suffix scan over the first kTileP lanes (nt <= kTileP)
+    if (tid < 64) {
+      const float gv = tid < nt ? sG[tid] : 0.f;
+      float x = gv;  // inclusive suffix sum
+#pragma unroll
+      for (int o = 1; o < kTileP; o <<= 1) {
+        const float y = __shfl_down(x, o);
+        if (tid + o < kTileP) x += y;
+      }
+      if (tid < nt) sW[tid] = __expf(carry + x - gv);
+    }
+    float tile_sum = 0.f;
+    for (int i = nt - 1; i >= 0; --i) tile_sum += sG[i];
+    __syncthreads();
+    for (int jj = nt - 1; jj >= 0; --jj) {
+      const float wv = sW[jj] * sV[jj][r];
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) accum[i] += wv * sK[jj][4 * cq + 8 * (i & ~3) + (i & 3)];
+    }
+    carry += tile_sum;
+    tile_end -= nt;
+    nt = min(kTileP, tile_end);
+    __syncthreads();
+    if (nt > 0) {
+      stage_path<E, DK>(a, s, h, v0, rows, hl, tile_end - nt, nt, sK, sV, sG);
+      __syncthreads();
+    }
+  }
+  const float gall = __expf(carry);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) S[i] = gall * S[i] + accum[i];
+
+  // flush the committed state (or keep the accepted tokens as history, above)
+  float* stores[2] = {flush ? a.ckpt : nullptr, a.state_out};
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    if (!stores[w] || !row_ok) continue;
+    float* dst = stores[w] + ((size_t)s * H + h) * SS + (size_t)(v0 + r) * DK + 4 * cq;
+#pragma unroll
+    for (int i = 0; i < CPT; i += 4)
+      *reinterpret_cast<float4*>(dst + 8 * i) = make_float4(S[i], S[i + 1], S[i + 2], S[i + 3]);
+  }
+  if (h == 0 && vb == 0 && tid == 0) a.hist_len_out[s] = flush ? 0 : L;
+
+  // verify the new draft from S
   E* og = reinterpret_cast<E*>(a.out);
   for (int t = 0; t < N; ++t) {
-    const float* kt = dK + (size_t)t * DK + cq * CPT;
-    const float* qt = dQ + (size_t)t * DK + cq * CPT;
+    const float* kt = dK + (size_t)t * DK + 4 * cq;
+    const float* qt = dQ + (size_t)t * DK + 4 * cq;
     float u = 0.f;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) u += S[i] * kt[i];
+    for (int i = 0; i < CPT; ++i) u += S[i] * kt[8 * (i & ~3) + (i & 3)];
     u += __shfl_xor(u, 1);
     u += __shfl_xor(u, 2);
     u += __shfl_xor(u, 4);
@@ -224,8 +286,9 @@ __global__ void __launch_bounds__(kThr) k_chain_step(const ChainArgs a) {
     float o = 0.f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      S[i] = al * S[i] + vt * kt[i];
-      o += S[i] * qt[i];
+      const int c = 8 * (i & ~3) + (i & 3);
+      S[i] = al * S[i] + vt * kt[c];
+      o += S[i] * qt[c];
     }
     o += __shfl_xor(o, 1);
     o += __shfl_xor(o, 2);

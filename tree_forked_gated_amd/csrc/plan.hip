@@ -43,6 +43,19 @@ __device__ inline int seg_of(const int* seg_start, int n_seg, int t) {
   return lo;
 }
 
+constexpr int kBkoLevels = 16;  // levels whose length-bucket offsets are formed in LDS
+
+// Exclusive prefix sum over the 64 lanes of a wave.
+__device__ inline int wave_excl_scan(int v) {
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if ((threadIdx.x & 63) >= o) x += y;
+  }
+  return x - v;
+}
+
 // True when seq_start failed validation: later kernels must not index with it.
 __device__ inline bool bad_csr(const Meta& m) { return (*m.err >> 32) == (unsigned long long)GDN_DEV_SEQ_START; }
 
@@ -345,6 +358,12 @@ __global__ void __launch_bounds__(256) k_finish(const int* parent, const int* se
       run += tot;
     }
     if (threadIdx.x == 0) lptr[max_levels] = run;
+    // offsets of the length buckets inside each level (one wave per level, one bucket per lane)
+    __shared__ int s_bko[kBkoLevels][kLenBuckets];
+    const bool bko = max_levels <= kBkoLevels;
+    if (bko)
+      for (int lv = threadIdx.x >> 6; lv < max_levels; lv += 4)
+        s_bko[lv][threadIdx.x & 63] = wave_excl_scan(m.level_bkt[lv * kLenBuckets + (threadIdx.x & 63)]);
     __syncthreads();
     if (blockIdx.x == 0) {
       for (int l = threadIdx.x; l <= max_levels; l += 256) m.level_ptr[l] = lptr[l];
@@ -357,9 +376,13 @@ __global__ void __launch_bounds__(256) k_finish(const int* parent, const int* se
         // longest first: the entries of longer buckets of the level come before
         const int nch = m.seg_mode[i] ? 1 : (m.seg_len[i] + kChunk - 1) / kChunk;
         const int bk = len_bucket(nch);
-        const int* cnt = m.level_bkt + lv * kLenBuckets;
         int pos = lptr[lv];
-        for (int b = 0; b < bk; ++b) pos += cnt[b];
+        if (bko) {
+          pos += s_bko[lv][bk];
+        } else {
+          const int* cnt = m.level_bkt + lv * kLenBuckets;
+          for (int b = 0; b < bk; ++b) pos += cnt[b];
+        }
         pos += atomicAdd(&m.level_fill[lv * kLenBuckets + bk], 1);
         m.level_items[pos] = i;
         m.unit_info[pos] = make_int4(m.seg_start[i], m.seg_len[i], m.seg_mode[i] | (m.seg_seq[i] << 1),
@@ -649,6 +672,13 @@ __global__ void __launch_bounds__(kPT) k_plan_small(const int* parent, const int
     m.level_ptr[max_levels] = run;
     *m.plan_tag = tag;
   }
+  // offsets of the length buckets inside each level (wave w: level w, one bucket per lane)
+  __shared__ int s_bko[kBkoLevels][kLenBuckets];
+  const bool bko = max_levels <= kBkoLevels;
+  if (bko && (tid >> 6) < max_levels) {
+    const int lv = tid >> 6, b = tid & 63;
+    s_bko[lv][b] = wave_excl_scan(ld_l2(m.level_bkt + lv * kLenBuckets + b));
+  }
   __syncthreads();
   if (!bad) {
     for (int i = tid; i < n_seg; i += kPT) {
@@ -656,9 +686,13 @@ __global__ void __launch_bounds__(kPT) k_plan_small(const int* parent, const int
       if (lv < max_levels) {
         const int nch = m.seg_mode[i] ? 1 : (m.seg_len[i] + kChunk - 1) / kChunk;
         const int bk = len_bucket(nch);
-        const int* cnt = m.level_bkt + lv * kLenBuckets;
         int pos = m.level_ptr[lv];
-        for (int b = 0; b < bk; ++b) pos += ld_l2(cnt + b);
+        if (bko) {
+          pos += s_bko[lv][bk];
+        } else {
+          const int* cnt = m.level_bkt + lv * kLenBuckets;
+          for (int b = 0; b < bk; ++b) pos += ld_l2(cnt + b);
+        }
         pos += atomicAdd(&m.level_fill[lv * kLenBuckets + bk], 1);
         m.level_items[pos] = i;
         m.unit_info[pos] = make_int4(segs[i], m.seg_len[i], m.seg_mode[i] | (m.seg_seq[i] << 1), m.seg_slot[i]);
@@ -681,12 +715,27 @@ __global__ void __launch_bounds__(kPT) k_plan_small(const int* parent, const int
       }
     }
     const int lane = tid & 63;
-    for (int s = tid >> 6; s < n_seq; s += kPT / 64) {
+    // four sequences per wave and round: their parents are loaded before any is used
+    for (int s0 = tid >> 6; s0 < n_seq; s0 += 4 * (kPT / 64)) {
+      int gp[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = s0 + u * (kPT / 64);
+        gp[u] = -1;
+        if (s < n_seq) {
+          const int a = ss[s], n = ss[s + 1] - a;
+          if (n > 0 && n <= kChunk && lane < n) gp[u] = parent[a + lane];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+      const int s = s0 + u * (kPT / 64);
+      if (s >= n_seq) break;
       const int a = ss[s], n = ss[s + 1] - a;
       if (n <= 0 || n > kChunk) continue;
       int p = -1;
       if (lane < n) {
-        const int g = parent[a + lane];
+        const int g = gp[u];
         p = (g >= a && g < a + lane) ? g - a : -1;
       }
       unsigned long long anc = (lane < n) ? (1ull << lane) : 0ull;
@@ -705,6 +754,7 @@ __global__ void __launch_bounds__(kPT) k_plan_small(const int* parent, const int
       if (lane < n) {
         m.tree_mask[(size_t)s * kChunk + lane] = anc;
         m.depth[a + lane] = d;
+      }
       }
     }
   }
