@@ -71,6 +71,30 @@ def test_mixed_forest_bf16():
     _check(wl, "mixed")
 
 
+def test_short_sequences_with_rows_bf16():
+    """Every sequence fits one chunk (the planner's one-pass path): readout rows
+    in shuffled order, state rows at leaves and inner nodes, an empty sequence
+    and one-token sequences among draft trees of up to 64 tokens."""
+    rng = np.random.default_rng(41)
+    sizes = [64, 1, 0, 37, 64, 2, 17, 50, 1]
+    parents, starts, used = [], [0], 0
+    for n in sizes:
+        lp = W.random_draft_tree(rng, n) if n else np.zeros(0, np.int32)
+        parents.append(np.where(lp < 0, -1, lp + used).astype(np.int32))
+        used += n
+        starts.append(used)
+    parent = np.concatenate(parents).astype(np.int32)
+    seq_start = np.array(starts, np.int32)
+    T, H, D = used, 2, 128
+    q, k, v, beta, g = W._values(rng, T, H, D, D, "bf16")
+    init = W._init(rng, len(sizes), H, D, D, True)
+    out_rows = rng.permutation(T)[: T // 2].astype(np.int32)
+    inner = np.setdiff1d(np.unique(parent[parent >= 0]), W.leaves_of(parent))[:9]
+    state_rows = rng.permutation(np.concatenate([W.leaves_of(parent), inner])).astype(np.int32)
+    wl = W.Workload("short_rows", "bf16", parent, seq_start, q, k, v, beta, g, init, out_rows, state_rows)
+    _check(wl, "short_rows")
+
+
 @pytest.mark.parametrize("n_nodes", [1, 2, 17, 63, 64])
 def test_tree_chunk_sizes_fp32(n_nodes):
     wl = W.draft_trees(n_seq=3, n_nodes=n_nodes, H=1, D=16)

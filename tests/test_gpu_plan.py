@@ -36,6 +36,30 @@ def _compare(parent, seq_start, **kw):
     return got, ref
 
 
+def _trees(sizes, seed=5):
+    """Draft trees of the given sizes (0 for an empty sequence), local parents."""
+    rng = np.random.default_rng(seed)
+    parents, starts, used = [], [0], 0
+    for n in sizes:
+        lp = W.random_draft_tree(rng, n) if n else np.zeros(0, np.int32)
+        parents.append(np.where(lp < 0, -1, lp + used).astype(np.int32))
+        used += n
+        starts.append(used)
+    return np.concatenate(parents).astype(np.int32), np.array(starts, np.int32)
+
+
+def test_plan_short_sequences_with_rows():
+    """The one-pass path: every sequence fits one chunk (empty and one-token
+    sequences among them), with readout and state rows."""
+    parent, seq = _trees([64, 1, 0, 37, 64, 2, 17, 50, 1, 0])
+    T = parent.shape[0]
+    rng = np.random.default_rng(6)
+    say(f"plan short sequences T={T}")
+    got, _ = _compare(parent, seq, out_rows=rng.permutation(T)[:90].astype(np.int32),
+                      state_rows=rng.permutation(T)[:40].astype(np.int32))
+    assert got["n_fork"] == 0 and got["n_seg"] == 8
+
+
 def test_plan_tiny_tree():
     wl = W.tiny_tree()
     say("plan tiny_tree")
@@ -68,14 +92,18 @@ def test_plan_full_size_structures():
 
 @pytest.mark.parametrize("case", ["order", "self", "below", "crossseq", "seqstart", "seqlast", "noseq", "forkcap",
                                   "levelcap", "rowdup", "rowrange"])
-@pytest.mark.parametrize("long", [False, True])
-def test_plan_errors_match(case, long):
-    """Short streams are planned by one workgroup, long ones by six launches:
-    both report the same first error as the reference planner."""
-    wl = W.random_small(11, n_seq=4, H=1, Dk=16, Dv=16, max_len=200)
-    parent = wl.parent.copy()
-    seq = wl.seq_start.copy()
-    if long:  # a 5000-token chain appended as a fifth sequence
+@pytest.mark.parametrize("shape", ["mixed", "long", "trees"])
+def test_plan_errors_match(case, shape):
+    """Short streams are planned by one workgroup (in one pass when every
+    sequence fits one chunk), long ones by six launches: all report the same
+    first error as the reference planner."""
+    if shape == "trees":
+        parent, seq = _trees([9, 30, 0, 64, 5, 1])
+    else:
+        wl = W.random_small(11, n_seq=4, H=1, Dk=16, Dv=16, max_len=200)
+        parent = wl.parent.copy()
+        seq = wl.seq_start.copy()
+    if shape == "long":  # a 5000-token chain appended as a fifth sequence
         T0 = wl.T
         chain = np.arange(T0 - 1, T0 + 4999, dtype=np.int32)
         chain[0] = -1
@@ -109,7 +137,7 @@ def test_plan_errors_match(case, long):
         kw = {"out_rows": np.array([1, 2, 1], np.int32)}
     elif case == "rowrange":
         kw = {"state_rows": np.array([0, T], np.int32)}
-    say(f"plan error case {case} long={long} T={T}")
+    say(f"plan error case {case} shape={shape} T={T}")
     got, ref = _compare(parent, seq, **kw)
     if case not in ("forkcap", "levelcap") or ref["error"] != (0, 0):
         assert ref["error"] != (0, 0)

@@ -474,18 +474,291 @@ __device__ inline int wg_excl_scan(int v, int* sh, int* total) {
 // issue four tokens' loads before using any of them.
 constexpr int kSeqLds = 2048;  // sequence starts held in LDS (n_seq + 1 entries)
 constexpr int kSegLds = 4096;  // segment starts held in LDS
+static_assert(kSegLds <= kSmallPlanT, "segment starts share the short path's buffer");
+
+// ---- streams of short sequences (draft trees)
+//
+// When every sequence holds at most 64 tokens, each one is a single tree chunk:
+// one segment per non-empty sequence, in stream order, all at level 0, no fork
+// tokens and no fork slots. The tables then follow from each sequence's bounds
+// and parents alone, and only the row maps need two passes (map, then the
+// check for repeats). The tables are those the general steps write for such a
+// stream, except the planner's own start and fork flags, which only its
+// general steps read. Everything is formed from one round of loads; threads
+// exchange data through LDS only, so the barriers wait for LDS traffic alone
+// and never for the global stores in flight, and the first error is kept in
+// LDS and stored at the end. (Stage stamps on an MI355X, 64 trees of 64
+// tokens: with ordinary barriers, per-token sequence lookups and a mask pass of
+// its own, the barriers waited about 1.5 us for stores, and the lookups and the
+// mask pass took 2.2 and 4 us.)
+__device__ inline void lds_raise(unsigned long long* e, int code, long long index) {
+  atomicMin(e, ((unsigned long long)(unsigned)code << 32) | (unsigned long long)(uint32_t)index);
+}
+
+// Workgroup barrier that orders LDS traffic only (global stores stay in flight).
+__device__ inline void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Exclusive scan over the workgroup with LDS-only barriers.
+__device__ inline int short_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) sh[w] = x;
+  lds_sync();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < kPT / 64; ++k) {
+    const int c = sh[k];
+    base += k < w ? c : 0;
+    tot += c;
+  }
+  *total = tot;
+  return base + x - v;
+}
+
+constexpr int kShortPer = kSmallPlanT / kPT;  // tokens (and rows) per thread
+
+// The short path's loads, issued at the kernel's start right after those of
+// seq_start: the parents of tokens tid + u kPT and the rows at those positions.
+struct ShortLoads {
+  int pv[kShortPer], ro[kShortPer], rs[kShortPer];
+};
+
+__device__ inline ShortLoads short_loads(const int* parent, int T, const int* out_rows, int n_out, const int* state_rows,
+                                         int n_state) {
+  ShortLoads L;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kShortPer; ++u) {
+    const int i = tid + u * kPT;
+    L.pv[u] = i < T ? parent[i] : -1;
+    L.ro[u] = (out_rows && i < n_out) ? out_rows[i] : -1;
+    L.rs[u] = (state_rows && i < n_state) ? state_rows[i] : -1;
+  }
+  return L;
+}
+
+__device__ void plan_short(const ShortLoads& L, const int* ss, int n_seq, int T, bool no_empty, const int* out_rows,
+                           int n_out, const int* state_rows, int n_state, int max_levels, unsigned long long tag,
+                           const Meta& m, int* s_out, int* s_st, int* s_par, int* sh, unsigned long long* s_err) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  constexpr int kPer = kShortPer;
+  constexpr int kW = kPT / 64;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int t = tid + u * kPT;
+    if (t < T) {
+      s_par[t] = L.pv[u];
+      s_out[t] = kUnmapped;
+      s_st[t] = kUnmapped;
+    }
+  }
+  if (tid == 0) *s_err = kNoError;
+  lds_sync();
+  // requested rows: the first position asking for a token owns it
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * kPT;
+    if (out_rows && i < n_out) {
+      if (L.ro[u] < 0 || L.ro[u] >= T) lds_raise(s_err, GDN_DEV_ROWS, i);
+      else atomicMin(&s_out[L.ro[u]], i);
+    }
+    if (state_rows && i < n_state) {
+      if (L.rs[u] < 0 || L.rs[u] >= T) lds_raise(s_err, GDN_DEV_ROWS, i);
+      else atomicMin(&s_st[L.rs[u]], i);
+    }
+  }
+  if (out_rows)
+    for (int i = tid + kPer * kPT; i < n_out; i += kPT) {
+      const int r = out_rows[i];
+      if (r < 0 || r >= T) lds_raise(s_err, GDN_DEV_ROWS, i);
+      else atomicMin(&s_out[r], i);
+    }
+  if (state_rows)
+    for (int i = tid + kPer * kPT; i < n_state; i += kPT) {
+      const int r = state_rows[i];
+      if (r < 0 || r >= T) lds_raise(s_err, GDN_DEV_ROWS, i);
+      else atomicMin(&s_st[r], i);
+    }
+  // one wave per sequence, four sequences of a wave at a time: the token
+  // tables, the parent checks, and the ancestor-or-self masks and depths by
+  // pointer jumping (the four sequences' shuffles overlap; the jumps stop once
+  // every token has reached its root)
+  for (int s0 = tid >> 6; s0 < n_seq; s0 += 4 * kW) {
+    int a[4], n[4], p[4];
+    unsigned long long anc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sq = s0 + u * kW;
+      a[u] = 0;
+      n[u] = 0;
+      if (sq < n_seq) {
+        a[u] = ss[sq];
+        n[u] = ss[sq + 1] - a[u];
+      }
+      p[u] = -1;
+      if (lane < n[u]) {
+        const int t = a[u] + lane;
+        const int g = s_par[t];
+        if (g < -1 || g >= t) lds_raise(s_err, GDN_DEV_PARENT_ORDER, t);
+        else if (g >= 0 && g < a[u]) lds_raise(s_err, GDN_DEV_PARENT_SEQ, t);
+        p[u] = (g >= a[u] && g < t) ? g - a[u] : -1;
+        m.tok_seq[t] = sq;
+        m.fork_slot[t] = -1;
+      }
+      anc[u] = (lane < n[u]) ? (1ull << lane) : 0ull;
+    }
+    for (int r = 0; r < 6; ++r) {
+      if (!__any(p[0] >= 0 || p[1] >= 0 || p[2] >= 0 || p[3] >= 0)) break;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int src = p[u] >= 0 ? p[u] : lane;
+        const unsigned long long panc = __shfl(anc[u], src);
+        const int pp = __shfl(p[u], src);
+        if (p[u] >= 0) {
+          anc[u] |= panc;
+          p[u] = pp;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sq = s0 + u * kW;
+      if (sq >= n_seq) break;
+      m.tree_mask[(size_t)sq * kChunk + lane] = anc[u];
+      if (lane < n[u]) m.depth[a[u] + lane] = __popcll(anc[u]) - 1;  // ancestors in the chunk
+    }
+  }
+  // segments: the non-empty sequences in order (two sequences per thread),
+  // numbered by a scan unless no sequence is empty; the barrier (the scan's
+  // own, or one of its own) orders the row atomics before the checks below
+  int ne0 = 0, ne1 = 0;
+  const int s0 = 2 * tid;
+  if (s0 < n_seq) ne0 = ss[s0 + 1] > ss[s0];
+  if (s0 + 1 < n_seq) ne1 = ss[s0 + 2] > ss[s0 + 1];
+  int n_seg = n_seq, e = s0;
+  if (no_empty) lds_sync();
+  else e = short_scan(ne0 + ne1, sh, &n_seg);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int sq = s0 + u;
+    if (!(u ? ne1 : ne0)) continue;
+    const int i = e + (u ? ne0 : 0);
+    const int a = ss[sq], n = ss[sq + 1] - a;
+    m.seg_start[i] = a;
+    m.seg_len[i] = n;
+    m.seg_seq[i] = sq;
+    m.seg_mode[i] = 1;
+    m.seg_entry[i] = -1;
+    m.seg_slot[i] = -1;
+    m.seg_level[i] = 0;
+    m.seg_depth0[i] = 0;
+    m.level_items[i] = i;
+    m.unit_info[i] = make_int4(a, n, 1 | (sq << 1), -1);
+  }
+  // repeats among the requested rows, and the row maps
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * kPT;
+    if (out_rows && i < n_out && L.ro[u] >= 0 && L.ro[u] < T && s_out[L.ro[u]] != i) lds_raise(s_err, GDN_DEV_ROWS, i);
+    if (state_rows && i < n_state && L.rs[u] >= 0 && L.rs[u] < T && s_st[L.rs[u]] != i)
+      lds_raise(s_err, GDN_DEV_ROWS, i);
+  }
+  if (out_rows)
+    for (int i = tid + kPer * kPT; i < n_out; i += kPT) {
+      const int r = out_rows[i];
+      if (r >= 0 && r < T && s_out[r] != i) lds_raise(s_err, GDN_DEV_ROWS, i);
+    }
+  if (state_rows)
+    for (int i = tid + kPer * kPT; i < n_state; i += kPT) {
+      const int r = state_rows[i];
+      if (r >= 0 && r < T && s_st[r] != i) lds_raise(s_err, GDN_DEV_ROWS, i);
+    }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int t = tid + u * kPT;
+    if (t < T) {
+      m.out_map[t] = s_out[t];
+      m.state_map[t] = s_st[t];
+    }
+  }
+  // levels: every segment at level 0 and one chunk long
+  const int one = len_bucket(1);
+  for (int l = tid; l <= max_levels; l += kPT) {
+    m.level_ptr[l] = l == 0 ? 0 : n_seg;
+    if (l < max_levels) m.level_count[l] = l == 0 ? n_seg : 0;
+  }
+  for (int i = tid; i < max_levels * kLenBuckets; i += kPT) {
+    const int v = (i == one) ? n_seg : 0;  // level 0, bucket of one chunk
+    m.level_bkt[i] = v;
+    m.level_fill[i] = v;
+  }
+  for (int i = tid; i < max_levels * kSchedInts; i += kPT) {
+    const int q = i % kSchedInts;
+    const bool used = i < kSchedInts && n_seg > 0;
+    m.walk_ctr[i] = q < kWalkQueues ? 0 : q == kWalkQueues ? (used ? 1 : 0x7fffffff) : (used ? 1 : 0);
+  }
+  lds_sync();  // every error raised
+  if (tid == 0) {
+    *m.err = *s_err;
+    *m.n_seg = n_seg;
+    *m.n_fork = 0;
+    *m.plan_tag = tag;
+  }
+}
 
 __global__ void __launch_bounds__(kPT) k_plan_small(const int* parent, const int* seq_start, int n_seq, int T,
                                                     const int* out_rows, int n_out, const int* state_rows, int n_state,
                                                     int max_forks, int max_levels, unsigned long long tag, Meta m) {
   __shared__ int sh[kPT / 64 + 1];
   __shared__ int s_ss[kSeqLds + 1];
-  __shared__ int s_seg[kSegLds];
+  __shared__ int s_big[3 * kSmallPlanT];  // segment starts; on the short path the row maps and the parents
+  __shared__ unsigned long long s_err;
+  __shared__ int s_flag;
+  int* s_seg = s_big;
   const int tid = threadIdx.x;
   const bool ss_lds = n_seq <= kSeqLds;
   const int* ss = ss_lds ? s_ss : seq_start;
-  if (ss_lds)
-    for (int i = tid; i <= n_seq; i += kPT) s_ss[i] = seq_start[i];
+  if (ss_lds) {
+    // seq_start first, then the short path's loads, so that the wait for the
+    // former does not include the latter
+    int sv[kSeqLds / kPT + 1];
+#pragma unroll
+    for (int k = 0; k <= kSeqLds / kPT; ++k) {
+      const int i = tid + k * kPT;
+      sv[k] = i <= n_seq ? seq_start[i] : 0;
+    }
+    const ShortLoads sl = short_loads(parent, T, out_rows, n_out, state_rows, n_state);
+#pragma unroll
+    for (int k = 0; k <= kSeqLds / kPT; ++k) {
+      const int i = tid + k * kPT;
+      if (i <= n_seq) s_ss[i] = sv[k];
+    }
+    if (tid == 0) s_flag = 3;
+    lds_sync();
+    // a valid seq_start whose sequences all fit one chunk takes the short path
+    // (bit 0 of the flag), noting whether some sequence is empty (bit 1 clear)
+    int ok = 1, full = 1;
+    for (int s = tid; s <= n_seq; s += kPT) {
+      const int v = s_ss[s];
+      if (s == 0 ? v != 0 : (v < s_ss[s - 1] || v > T || v - s_ss[s - 1] > kChunk)) ok = 0;
+      if (s == n_seq && v != T) ok = 0;
+      if (s > 0 && v == s_ss[s - 1]) full = 0;
+    }
+    if (!ok) atomicAnd(&s_flag, ~1);
+    if (!full) atomicAnd(&s_flag, ~2);
+    lds_sync();
+    const int flag = s_flag;
+    if (flag & 1) {
+      plan_short(sl, s_ss, n_seq, T, (flag & 2) != 0, out_rows, n_out, state_rows, n_state, max_levels, tag, m, s_big,
+                 s_big + kSmallPlanT, s_big + 2 * kSmallPlanT, sh, &s_err);
+      return;
+    }
+  }
   // -- clear (as k_init)
   for (int i = tid; i < T; i += kPT) {
     m.tok_seq[i] = 0;
