@@ -16,7 +16,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdn_tree.so")
+# GDN_TREE_LIB names another build of the same library (the stage-stamp
+# measurement build, stage_stamps.py); by default the one beside this file.
+LIB_PATH = os.environ.get("GDN_TREE_LIB") or os.path.join(_HERE, "libgdn_tree.so")
 
 GDN_F32, GDN_BF16 = 0, 1
 DEV_ERRORS = {0: "ok", 1: "seq_start", 2: "parent order", 3: "parent in another sequence", 4: "fork capacity",

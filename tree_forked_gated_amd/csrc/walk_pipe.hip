@@ -45,6 +45,28 @@
 namespace gdn {
 namespace {
 
+// Stage stamps, in a measurement build only (compiled with -DGDN_WALK_STAMPS;
+// the library itself has none): s_memtime at the stage boundaries of every wave
+// of the first kStampWg workgroups, over the first kStampIts chunks of the
+// first level launch, read back with gdn_walk_stamps(). Lane 0 stores them
+// with ordinary vector stores.
+#ifdef GDN_WALK_STAMPS
+constexpr int kStampWg = 8, kStampWaves = 4, kStampIts = 128, kStampPts = 10;
+__device__ unsigned long long g_walk_stamps[kStampWg * kStampWaves * kStampIts * kStampPts];
+#define WALK_STAMP(IT, S)                                                                                   \
+  do {                                                                                                      \
+    const int w_ = (int)(threadIdx.x >> 6), i_ = (IT);                                                     \
+    if (blockIdx.x < kStampWg && a.level == 0 && i_ >= 0 && i_ < kStampIts && (threadIdx.x & 63) == 0 &&    \
+        w_ < kStampWaves)                                                                                   \
+      g_walk_stamps[(((int)blockIdx.x * kStampWaves + w_) * kStampIts + i_) * kStampPts + (S)] =           \
+          __builtin_amdgcn_s_memtime();                                                                     \
+  } while (0)
+#else
+#define WALK_STAMP(IT, S) \
+  do {                    \
+  } while (0)
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -709,6 +731,7 @@ __device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, 
   // Iteration -1 forms the products of chunk 0 while the state waves wait.
   for (int it = -1;; ++it) {
     if (it >= 0 && !rfl(reinterpret_cast<const Desc*>(smem + C::oTB + (it % 3) * kTB + tD)->valid)) break;
+    WALK_STAMP(it + 1, 0);
     const int s1 = (it + 1) % 3, s2 = (it + 2) % 3;
     unsigned char* tb1 = smem + C::oTB + s1 * kTB;
     const Desc nd = uniform_desc(nds[it & 1]);                              // chunk it + 2: K, Q, tables
@@ -718,17 +741,21 @@ __device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, 
     if (hid == 1 && nx.valid) issue_v<BV>(a, nx, smem + C::oV + ((it + 1) & 1) * C::VT, lane);
     Touch touch = {0u, 0u};
     if (nx.valid && nx.first && nx.sin) touch = prefetch_entry<BV>(nx.sin, hid, lane);
+    WALK_STAMP(it + 1, 1);
     if (nx.valid)
       chunk_products(hid, nx, smem + C::oKQ + s1 * 32768, tb1, smem + C::oPR + ((it + 1) & 1) * kPR,
                      smem + C::oPP + s1 * kPP, lt, lane);
+    WALK_STAMP(it + 1, 2);
     wait_vm();  // this wave's copies, token values and unit record have landed
     consume(touch);
+    WALK_STAMP(it + 1, 3);
     if (hid == 1) store_tokens(a, nd, tr, smem + C::oTB + s2 * kTB, lane);
     if (hid == 0) {
       Desc nn = {};
       if (nd.valid) nn = feed_next<BV>(ff, fr, a, xcd, count, base, lane);
       put_desc(reinterpret_cast<unsigned char*>(nds + ((it + 1) & 1)), nn, lane);
     }
+    WALK_STAMP(it + 1, 4);
     lds_barrier();
   }
 }
@@ -852,6 +879,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
         for (int r = 0; r < 4; ++r) ST[nb][dt][r] *= cs;
   }
   stage_fence<NB>();
+  WALK_STAMP(it, 1);
   // e^G S_e Q^T (the output, transposed): lane holds four columns of one token
   f32x4 O[NB][4];
   if (HAS_OUT) {
@@ -872,6 +900,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
     }
   }
   stage_fence<NB>();
+  WALK_STAMP(it, 2);
   // R = beta (V - e^G K S^T) in place of X
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
@@ -887,6 +916,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
     }
   }
   stage_fence<NB>();
+  WALK_STAMP(it, 3);
   // block substitution with the helpers' -A_bm and (I + A_bb)^{-1}
   bf16x4 nA[6], DI[4];
 #pragma unroll
@@ -913,6 +943,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
     Vb[nb][3] = to_bf4(Vt[nb][3]);
   }
   stage_fence<NB>();
+  WALK_STAMP(it, 4);
   if (HAS_OUT) {
     // O^T += Vt^T P^T over pairs of 16-token blocks (blocks of P above the
     // diagonal are zero; the helpers' P fragments are the B operands)
@@ -952,6 +983,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
     }
   }
   stage_fence<NB>();
+  WALK_STAMP(it, 5);
   if (a.pv) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -971,6 +1003,7 @@ __device__ __forceinline__ void state_chunk(const Args& a, const unsigned char* 
     }
   }
   stage_fence<NB>();
+  WALK_STAMP(it, 6);
   // states after requested tokens (fork slots, state rows) and at the chunk exit
   if (!todo) return;
   const float* sG2 = reinterpret_cast<const float*>(tb + tG2);
@@ -1112,6 +1145,7 @@ __device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, i
   for (int it = 0;; ++it) {
     const unsigned char* tb = smem + C::oTB + (it % 3) * kTB;
     if (!cd.valid) break;
+    WALK_STAMP(it, 0);
     const int t0 = cd.t0, n = cd.n, h = cd.h, v0 = cd.v0;
     const int mode = cd.mode;
     const bool has_out = cd.has_out, need_exit = cd.need_exit, first = cd.first;
@@ -1132,9 +1166,12 @@ __device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, i
       state_chunk<BV, true>(a, smem, tb, kq, vt, pr, o, ST, Sb, it, t0, n, h, v0w, mode, need_exit, todo, lane);
     else
       state_chunk<BV, false>(a, smem, tb, kq, vt, pr, o, ST, Sb, it, t0, n, h, v0w, mode, need_exit, todo, lane);
+    WALK_STAMP(it, 7);
     const Desc* dn = reinterpret_cast<const Desc*>(smem + C::oTB + ((it + 1) % 3) * kTB + tD);
     cd = load_sdesc(reinterpret_cast<const unsigned char*>(dn));
+    WALK_STAMP(it, 8);
     if (cd.valid && cd.first) load_entry<NB>(dn, ws, lane, ST);
+    WALK_STAMP(it, 9);
     lds_barrier();
   }
 }
@@ -1252,3 +1289,15 @@ hipError_t launch_walk_pipe(const gdn_tree_fwd_args& fa, const Meta& m, int bv, 
 }
 
 }  // namespace gdn
+
+#ifdef GDN_WALK_STAMPS
+// Measurement build only: copies (clear = 0) or zeroes (clear != 0) the stamps.
+extern "C" int gdn_walk_stamps(unsigned long long* host, int clear) {
+  constexpr size_t n = sizeof(gdn::g_walk_stamps);
+  if (clear) {
+    static unsigned long long zero[n / sizeof(unsigned long long)];
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(gdn::g_walk_stamps), zero, n);
+  }
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(gdn::g_walk_stamps), n);
+}
+#endif
