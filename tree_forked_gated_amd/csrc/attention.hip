@@ -51,6 +51,7 @@ constexpr int oV = 2 * kTileB;          // [2] V tiles
 constexpr int oSp = 4 * kTileB;         // the item's spans (int2)
 constexpr int kLds = oSp + 8 * kMaxSpans;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.f;  // a row's weights stay below 2^kLazy before its reference moves
 
 struct AttnArgs {
   const __bf16* q;
@@ -266,22 +267,24 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
         }
         bf16x8 w01[HPW], w23[HPW];
         float alpha[HPW];
-        bool rescale[HPW];
+        bool rescale[HPW];  // wave-uniform: some query of the wave moved its reference
         // masks only where a tile is not fully visible (the diagonal tile, a span's last tile, tree tiles)
         const bool masked = cur.kind != 0 || cur.n < kT;
+        unsigned vis = 0xffffu;  // bit 4 kb + r: key 16 kb + 4 g4 + r is visible to query qi
+        if (masked) {
+          unsigned long long ok = cur.kind == 2 ? tmask : cur.kind == 1 ? (2ull << qi) - 1ull : ~0ull;
+          if (cur.n < kT) ok &= (1ull << cur.n) - 1ull;
+          const unsigned long long sh = ok >> (4 * g4);
+          vis = (unsigned)((sh & 0xfull) | ((sh >> 12) & 0xf0ull) | ((sh >> 24) & 0xf00ull) | ((sh >> 36) & 0xf000ull));
+        }
 #pragma unroll
         for (int j = 0; j < HPW; ++j) {
           if (masked) {
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int kk = 16 * kb + 4 * g4 + r;
-                bool ok = kk < cur.n;
-                if (cur.kind == 1) ok = ok && kk <= qi;
-                else if (cur.kind == 2) ok = ok && ((tmask >> kk) & 1ull);
-                if (!ok) S[j][kb][r] = -INFINITY;
-              }
+              for (int r = 0; r < 4; ++r)
+                if (!((vis >> (4 * kb + r)) & 1u)) S[j][kb][r] = -INFINITY;
           }
           // running maxima in the scaled log2 domain (scale > 0): m = c max(s)
           float mt = -INFINITY;
@@ -291,10 +294,15 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
             for (int r = 0; r < 4; ++r) mt = fmaxf(mt, S[j][kb][r]);
           mt = fmaxf(mt, __shfl_xor(mt, 16));
           mt = fmaxf(mt, __shfl_xor(mt, 32));
-          const float mn = fmaxf(m[j], mt * a.c);
+          // The reference m (scaled log2 domain) moves up only when this tile's
+          // maximum exceeds it by more than kLazy, so that the weights stay below
+          // 2^kLazy; softmax does not depend on the reference, and most tiles
+          // then leave the accumulators alone.
+          const float ms = mt * a.c;
+          const float mn = ms > m[j] + kLazy ? ms : m[j];
           const float mref = mn == -INFINITY ? 0.f : mn;
           alpha[j] = __builtin_amdgcn_exp2f(m[j] - mref);
-          rescale[j] = __builtin_amdgcn_ballot_w64(mn != m[j]) != 0ull;  // some query's maximum moved
+          rescale[j] = __builtin_amdgcn_ballot_w64(mn != m[j]) != 0ull;
           float ls = 0.f;
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
@@ -303,10 +311,23 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
               S[j][kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[j][kb][r], a.c, -mref));
               ls += S[j][kb][r];
             }
-          l[j] = rescale[j] ? l[j] * alpha[j] + ls : l[j] + ls;
+          l[j] = l[j] * alpha[j] + ls;  // alpha is exactly 1 where the reference stayed
           m[j] = mn;
           w01[j] = cat8b(to_bf4(S[j][0]), to_bf4(S[j][1]));
           w23[j] = cat8b(to_bf4(S[j][2]), to_bf4(S[j][3]));
+        }
+        // rescale the accumulators only on the (rare) tiles that moved a
+        // reference: a real branch (the empty asm keeps the compiler from
+        // turning it into selects on every tile)
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          if (rescale[j]) {
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) O[j][dt][r] *= alpha[j];
+          }
         }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
@@ -315,12 +336,7 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
           const bf16x8 v23 = cat8(tr_read(vp + 8192), tr_read(vp + 12288));
 #pragma unroll
           for (int j = 0; j < HPW; ++j) {
-            f32x4 o = O[j][dt];
-            if (rescale[j]) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) o[r] *= alpha[j];
-            }
-            o = mma32(v01, w01[j], o);
+            const f32x4 o = mma32(v01, w01[j], O[j][dt]);
             O[j][dt] = mma32(v23, w23[j], o);
           }
         }
