@@ -181,6 +181,7 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
     for (int dt = 0; dt < 8; ++dt) oT[dt] = r0 * 256 + ((((4 * (dt >> 1) + p) ^ swz(r0))) << 4) + ((dt & 1) << 3);
   }
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8 kOnes = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
   for (;;) {
     if (tid == 0) s_claim = atomicAdd(a.claim, 1);
@@ -232,13 +233,14 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
     wait_vm();
     lds_barrier();
     f32x4 O[HPW][8];
-    float m[HPW], l[HPW];
+    float m[HPW];
+    f32x4 L[HPW];  // row sums of the weights, formed on the matrix cores (every element the query's sum)
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) O[j][dt] = zero;
       m[j] = -INFINITY;
-      l[j] = 0.f;
+      L[j] = zero;
     }
     const bool active = 16 * w < nq;
     for (int it = 0; cur.valid; ++it) {
@@ -303,15 +305,10 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
           const float mref = mn == -INFINITY ? 0.f : mn;
           alpha[j] = __builtin_amdgcn_exp2f(m[j] - mref);
           rescale[j] = __builtin_amdgcn_ballot_w64(mn != m[j]) != 0ull;
-          float ls = 0.f;
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              S[j][kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[j][kb][r], a.c, -mref));
-              ls += S[j][kb][r];
-            }
-          l[j] = l[j] * alpha[j] + ls;  // alpha is exactly 1 where the reference stayed
+            for (int r = 0; r < 4; ++r) S[j][kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[j][kb][r], a.c, -mref));
           m[j] = mn;
           w01[j] = cat8b(to_bf4(S[j][0]), to_bf4(S[j][1]));
           w23[j] = cat8b(to_bf4(S[j][2]), to_bf4(S[j][3]));
@@ -327,7 +324,16 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
             for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
               for (int r = 0; r < 4; ++r) O[j][dt][r] *= alpha[j];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) L[j][r] *= alpha[j];
           }
+        }
+        // the weights' row sums: a block of ones times P^T (the same bf16 weights
+        // as the numerator's)
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          const f32x4 t = mma32(kOnes, w01[j], L[j]);
+          L[j] = mma32(kOnes, w23[j], t);
         }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
@@ -348,9 +354,7 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
     if (active && qi < nq) {
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
-        float lt = l[j] + __shfl_xor(l[j], 16);
-        lt += __shfl_xor(lt, 32);
-        const float inv = 1.f / lt;
+        const float inv = 1.f / L[j][0];
         __bf16* orow = a.out + ((size_t)(q0 + qi) * a.Hq + h0 + j) * D;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
