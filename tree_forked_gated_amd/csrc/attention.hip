@@ -42,14 +42,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int D = 128;        // head dimension
 constexpr int kT = 64;        // keys per tile, queries per chunk
-constexpr int kThr = 256;     // four waves
 constexpr int kTileB = kT * D * 2;  // bytes of one K or V tile (bf16)
 constexpr int kMaxLevels = 64;  // fork nesting levels an item's span list may hold
 constexpr int kMaxSpans = kMaxLevels + 1;  // plus the sequence's cached keys
-constexpr int oK = 0;                   // [2] K tiles
-constexpr int oV = 2 * kTileB;          // [2] V tiles
-constexpr int oSp = 4 * kTileB;         // the item's spans (int2)
-constexpr int kLds = oSp + 8 * kMaxSpans;
+constexpr int oK = 0;  // K tiles, then V tiles, then the item's spans (int2)
+__host__ __device__ constexpr int attn_lds(int nbuf) { return 2 * nbuf * kTileB + 8 * kMaxSpans; }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.f;  // a row's weights stay below 2^kLazy before its reference moves
 
@@ -75,7 +72,6 @@ __device__ __forceinline__ void dma16(const void* sbase, unsigned voff, uint32_t
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
                : "memory");
 }
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ uint32_t lds_addr_of(const unsigned char* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((const lds_void*)p));
@@ -106,34 +102,51 @@ __device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
 __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
 
 // Rows [row0, row0 + n) of one key/value head (row stride rs bytes) into a
-// tile: wave w copies the 4-row blocks 4 w .. 4 w + 3; lane (g4, l16) copies
-// row 4 blk + g4, piece l16 ^ swz(row) into slot l16. Rows at or past n are
-// zero-filled and never read from memory.
-__device__ __forceinline__ void issue_tile(const __bf16* head0, int row0, int n, unsigned rs, unsigned char* tile,
-                                           int w, int lane) {
+// tile: wave w copies the 4-row blocks kB w .. kB w + kB - 1 (kB = 16 / NW);
+// lane (g4, l16) fills slot l16 of row r = 4 blk + g4 with the row's piece
+// l16 ^ swz(r). Rows at or past n are copied from row n - 1 (finite values:
+// their keys are masked and their weights are zero), so that every wave issues
+// exactly kB copies per tile and the waits can count them.
+// vo_full holds the lane's offsets of a full tile (the same for every tile);
+// l0 is the tile's LDS address.
+template <int NW>
+__device__ __forceinline__ void issue_tile(const __bf16* head0, int row0, int n, unsigned rs, uint32_t l0, int w,
+                                           int lane, const unsigned (&vo_full)[16 / NW]) {
+  constexpr int kB = 16 / NW;
   const int g4 = lane >> 4, l16 = lane & 15;
-  const unsigned char* src = reinterpret_cast<const unsigned char*>(rfl_ptr(head0)) + (size_t)rfl(row0) * rs +
-                             (size_t)(16 * w) * rs;
+  const unsigned char* src = reinterpret_cast<const unsigned char*>(rfl_ptr(head0)) + (size_t)rfl(row0) * rs;
+  if (n == kT) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int blk = 4 * w + b;
-    const unsigned vo = g4 * rs + (unsigned)((l16 ^ ((g4 << 2) | (blk & 3))) << 4);
-    if (4 * blk + g4 < n) dma16(src, vo, lds_addr_of(tile + blk * 1024));
-    else *reinterpret_cast<uint4*>(tile + blk * 1024 + lane * 16) = make_uint4(0, 0, 0, 0);
-    src += (size_t)4 * rs;
+    for (int b = 0; b < kB; ++b) dma16(src, vo_full[b], l0 + (kB * w + b) * 1024);
+  } else {
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int blk = kB * w + b, r = 4 * blk + g4;
+      const unsigned vo = (unsigned)min(r, n - 1) * rs + (unsigned)((l16 ^ swz(r)) << 4);
+      dma16(src, vo, l0 + blk * 1024);
+    }
   }
+}
+
+// Wait until at most 0, 1 or 2 tiles' copies (of kPer each) of this wave are in flight.
+template <int kPer>
+__device__ __forceinline__ void wait_tiles(int pending) {
+  static_assert(kPer == 4 || kPer == 8, "copies per tile");
+  if (pending == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (pending == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPer) : "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPer) : "memory");
 }
 
 // One key tile of an item: its first key, valid keys, and mask kind.
 struct Tile {
   int valid, k0, n, kind;  // kind 0: no mask beyond n; 1: causal (the item's own chunk); 2: tree ancestor bits
-  int sp;                  // span index
+  int sp, end;             // span index and the span's last key
 };
 
 // The tile after (sp, k0) in the item's span list (spans in LDS; span `own` is
 // the item's own segment, a span before it the cached keys).
 __device__ __forceinline__ Tile next_tile(const int2* sps, int nsp, int own, int sp, int k0, int q0, int tree) {
-  Tile t = {0, 0, 0, 0, 0};
+  Tile t = {0, 0, 0, 0, 0, 0};
   while (sp < nsp) {
     const int2 s = sps[sp];
     if (k0 < 0) k0 = s.x;
@@ -141,6 +154,7 @@ __device__ __forceinline__ Tile next_tile(const int2* sps, int nsp, int own, int
       t.valid = 1;
       t.sp = rfl(sp);
       t.k0 = rfl(k0);
+      t.end = rfl(s.y);
       t.n = rfl(min(kT, s.y - k0 + 1));
       t.kind = rfl((sp == own && k0 == q0) ? (tree ? 2 : 1) : 0);
       return t;
@@ -151,22 +165,45 @@ __device__ __forceinline__ Tile next_tile(const int2* sps, int nsp, int own, int
   return t;
 }
 
+// The tile after t: inside t's span without reading the span list again.
+__device__ __forceinline__ Tile after(const Tile& t, const int2* sps, int nsp, int own, int q0, int tree) {
+  if (!t.valid) return t;
+  const int k0 = t.k0 + kT;
+  if (k0 <= t.end) {
+    Tile u = t;
+    u.k0 = k0;
+    u.n = min(kT, t.end - k0 + 1);
+    u.kind = (t.sp == own && k0 == q0) ? (tree ? 2 : 1) : 0;
+    return u;
+  }
+  return next_tile(sps, nsp, own, t.sp + 1, -1, q0, tree);
+}
+
 // HPW query heads of one key/value group per wave: every K and V fragment read
-// from LDS feeds HPW matrix products.
-template <int HPW, bool CACHE>
-__global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
+// from LDS feeds HPW matrix products. NW = 4 waves take 16 queries each (HPW
+// heads per item, two workgroups per CU, K/V tiles double-buffered); NW = 8
+// waves take 16 queries and one of two head pairs each (2 HPW heads per item
+// sharing every K/V tile, one workgroup per CU, a ring of four tiles so that
+// three are in flight while one is used).
+template <int HPW, int NW, bool CACHE>
+__global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const AttnArgs a) {
+  constexpr int kBuf = NW == 8 ? 4 : 2;  // K/V tile buffers
+  constexpr int kPer = 2 * (16 / NW);    // copies per wave and tile (K and V)
+  constexpr int kHW = HPW * (NW / 4);    // query heads per item
+  constexpr int oV_ = kBuf * kTileB, oSp_ = 2 * kBuf * kTileB;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_claim;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = rfl(tid >> 6);
+  const int wq = w & 3, wh = w >> 2;  // the wave's query block and head pair
   const int g4 = lane >> 4, l16 = lane & 15;
   if (*a.err != kNoError) return;  // structural error in the tree: nothing is computed
   const int n_items = *a.n_items;
-  const int HG = a.Hq / HPW;  // head groups of HPW query heads
+  const int HG = a.Hq / kHW;  // head groups of kHW query heads
   const long long total = (long long)n_items * HG;
   const int G = a.Hq / a.Hkv;
   const unsigned rs_kv = (unsigned)a.Hkv * (D * 2);
-  int2* sps = reinterpret_cast<int2*>(smem + oSp);
+  int2* sps = reinterpret_cast<int2*>(smem + oSp_);
   // A-operand rows of the K fragments (row l16 of a 16-key block, d 32 ks + 8 g4 .. + 7)
   int oF[4];
 #pragma unroll
@@ -182,14 +219,22 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
   }
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   const bf16x8 kOnes = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  // the lane's copy offsets within a full tile, and the LDS address of the shared buffer
+  unsigned vo_full[16 / NW];
+#pragma unroll
+  for (int b = 0; b < 16 / NW; ++b) {
+    const int r = 4 * ((16 / NW) * w + b) + g4;
+    vo_full[b] = (unsigned)r * rs_kv + (unsigned)((l16 ^ swz(r)) << 4);
+  }
+  const uint32_t lds0 = lds_addr_of(smem);
 
   for (;;) {
     if (tid == 0) s_claim = atomicAdd(a.claim, 1);
-    __syncthreads();
+    lds_barrier();  // (also: every wave is done with the previous item's spans and tiles)
     const long long idx = s_claim;
     if (idx >= total) break;
-    const int item = (int)(idx / HG), h0 = (int)(idx % HG) * HPW;
-    const int hk = h0 / G;
+    const int item = (int)(idx / HG), hg0 = (int)(idx % HG) * kHW, h0 = hg0 + wh * HPW;
+    const int hk = hg0 / G;  // the item's heads share one key/value head (G is a multiple of kHW)
     const int4 inf = a.item_info[item];
     const int q0 = rfl(inf.x), nq = rfl(inf.y), tree = rfl(inf.z & 1), sq = rfl(inf.z >> 1);
     // the sequence's cached keys, if any, come first (span 0), then the item's spans
@@ -202,7 +247,7 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
     const int nsp = rfl(min(inf.w, kMaxLevels)) + own;
     if (tid >= own && tid < nsp) sps[tid] = a.spans[(size_t)item * a.max_levels + tid - own];
     // this wave's 16 queries of each head as MFMA fragments (zero past the chunk's queries)
-    const int qi = 16 * w + l16;  // query within the chunk
+    const int qi = 16 * wq + l16;  // query within the chunk
     bf16x8 Qf[HPW][4];
     unsigned long long tmask = 0;
     {
@@ -223,15 +268,27 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
     const __bf16* v0p = a.v + (size_t)hk * D;
     const __bf16* kc0p = CACHE ? a.k_cache + (size_t)hk * D : k0p;
     const __bf16* vc0p = CACHE ? a.v_cache + (size_t)hk * D : v0p;
-    __syncthreads();  // spans in LDS
+    lds_barrier();  // spans in LDS
+    // the tile in use and the kBuf - 1 after it; the first kBuf - 1 are copied now
     Tile cur = next_tile(sps, nsp, own, 0, -1, q0, tree);
-    if (cur.valid) {
-      const bool cc = cur.sp < own;
-      issue_tile(cc ? kc0p : k0p, cur.k0, cur.n, rs_kv, smem + oK, w, lane);
-      issue_tile(cc ? vc0p : v0p, cur.k0, cur.n, rs_kv, smem + oV, w, lane);
+    Tile ahead[kBuf - 1];
+    {
+      Tile t = cur;
+#pragma unroll
+      for (int i = 0; i < kBuf - 1; ++i) {
+        ahead[i] = after(t, sps, nsp, own, q0, tree);
+        t = ahead[i];
+      }
     }
-    wait_vm();
-    lds_barrier();
+    auto issue = [&](const Tile& t, int buf) {
+      const bool cc = t.sp < own;
+      issue_tile<NW>(cc ? kc0p : k0p, t.k0, t.n, rs_kv, lds0 + oK + buf * kTileB, w, lane, vo_full);
+      issue_tile<NW>(cc ? vc0p : v0p, t.k0, t.n, rs_kv, lds0 + oV_ + buf * kTileB, w, lane, vo_full);
+    };
+    if (cur.valid) issue(cur, 0);
+#pragma unroll
+    for (int i = 0; i < kBuf - 2; ++i)
+      if (ahead[i].valid) issue(ahead[i], i + 1);
     f32x4 O[HPW][8];
     float m[HPW];
     f32x4 L[HPW];  // row sums of the weights, formed on the matrix cores (every element the query's sum)
@@ -242,18 +299,20 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
       m[j] = -INFINITY;
       L[j] = zero;
     }
-    const bool active = 16 * w < nq;
+    const bool active = 16 * wq < nq;
     for (int it = 0; cur.valid; ++it) {
-      const Tile nxt = next_tile(sps, nsp, own, cur.sp, cur.k0 + kT, q0, tree);
-      const int b = it & 1;
-      if (nxt.valid) {
-        const bool cc = nxt.sp < own;
-        issue_tile(cc ? kc0p : k0p, nxt.k0, nxt.n, rs_kv, smem + oK + (b ^ 1) * kTileB, w, lane);
-        issue_tile(cc ? vc0p : v0p, nxt.k0, nxt.n, rs_kv, smem + oV + (b ^ 1) * kTileB, w, lane);
-      }
+      // this tile's copies (every wave's) have landed, and every wave is done
+      // with the buffer the next copy goes to (the previous tile's)
+      int pending = 0;
+#pragma unroll
+      for (int i = 0; i < kBuf - 2; ++i) pending += ahead[i].valid;
+      wait_tiles<kPer>(pending);
+      lds_barrier();
+      const int b = it & (kBuf - 1);
+      if (ahead[kBuf - 2].valid) issue(ahead[kBuf - 2], (it + kBuf - 1) & (kBuf - 1));
       if (active) {
         const unsigned char* kt = smem + oK + b * kTileB;
-        const unsigned char* vt = smem + oV + b * kTileB;
+        const unsigned char* vt = smem + oV_ + b * kTileB;
         // S^T = K Q^T: lane (query l16, g4) holds keys 16 kb + 4 g4 + r
         f32x4 S[HPW][4];
 #pragma unroll
@@ -347,9 +406,10 @@ __global__ void __launch_bounds__(kThr, 2) k_fork_attn(const AttnArgs a) {
           }
         }
       }
-      wait_vm();  // the next tile has landed
-      lds_barrier();
-      cur = nxt;
+      cur = ahead[0];
+#pragma unroll
+      for (int i = 0; i < kBuf - 2; ++i) ahead[i] = ahead[i + 1];
+      ahead[kBuf - 2] = after(ahead[kBuf - 2], sps, nsp, own, q0, tree);
     }
     if (active && qi < nq) {
 #pragma unroll
@@ -551,15 +611,21 @@ hipError_t launch_attention(const gdn_attn_args& aa, const AttnLayout& A, hipStr
   x.max_levels = aa.dims.max_levels;
   x.c = aa.scale * kLog2e;
   // two query heads per wave when a key/value group has an even number of them; cached keys in a variant of their own
-  const bool two = (aa.dims.Hq / aa.dims.Hkv) % 2 == 0, cache = aa.cache_start != nullptr;
-  void (*kern)(const AttnArgs) = two ? (cache ? k_fork_attn<2, true> : k_fork_attn<2, false>)
-                                     : (cache ? k_fork_attn<1, true> : k_fork_attn<1, false>);
+  // eight waves and four query heads of a key/value group per item when the
+  // group has a multiple of four, else four waves and two heads (or one)
+  const int G = aa.dims.Hq / aa.dims.Hkv;
+  const bool cache = aa.cache_start != nullptr;
+  const bool eight = G % 4 == 0, two = G % 2 == 0;
+  void (*kern)(const AttnArgs) = eight ? (cache ? k_fork_attn<2, 8, true> : k_fork_attn<2, 8, false>)
+                                 : two ? (cache ? k_fork_attn<2, 4, true> : k_fork_attn<2, 4, false>)
+                                       : (cache ? k_fork_attn<1, 4, true> : k_fork_attn<1, 4, false>);
+  const int threads = eight ? 512 : 256, lds = attn_lds(eight ? 4 : 2);
   int cus = 0, occ = 1;
-  e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), kLds, kThr, &occ);
+  e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), lds, threads, &occ);
   if (e != hipSuccess) return e;
   e = current_device_cus(&cus);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(cus * occ), dim3(kThr), kLds, s, x);
+  hipLaunchKernelGGL(kern, dim3(cus * occ), dim3(threads), lds, s, x);
   return hipGetLastError();
 }
 
