@@ -246,8 +246,14 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
     }
     const int nsp = rfl(min(inf.w, kMaxLevels)) + own;
     if (tid >= own && tid < nsp) sps[tid] = a.spans[(size_t)item * a.max_levels + tid - own];
+    // A chunk of at most 32 queries on eight waves is split by key tiles: the
+    // waves of query blocks 2 and 3 take the odd tiles of blocks 0 and 1's
+    // queries (two tiles per step), and hand their softmax states over at the end.
+    const int S = (NW == 8 && nq <= 32) ? 2 : 1;  // tiles per step
+    const int par = S == 2 ? wq >> 1 : 0;          // the wave's tile within a step
+    const int qb = S == 2 ? wq & 1 : wq;           // the wave's query block
     // this wave's 16 queries of each head as MFMA fragments (zero past the chunk's queries)
-    const int qi = 16 * wq + l16;  // query within the chunk
+    const int qi = 16 * qb + l16;  // query within the chunk
     bf16x8 Qf[HPW][4];
     unsigned long long tmask = 0;
     {
@@ -269,26 +275,20 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
     const __bf16* kc0p = CACHE ? a.k_cache + (size_t)hk * D : k0p;
     const __bf16* vc0p = CACHE ? a.v_cache + (size_t)hk * D : v0p;
     lds_barrier();  // spans in LDS
-    // the tile in use and the kBuf - 1 after it; the first kBuf - 1 are copied now
-    Tile cur = next_tile(sps, nsp, own, 0, -1, q0, tree);
-    Tile ahead[kBuf - 1];
-    {
-      Tile t = cur;
+    // a window of kBuf consecutive tiles: the step's S tiles first; the first
+    // kBuf - S are copied now (tile g + i of the item goes to buffer (g + i) mod kBuf)
+    Tile tw[kBuf];
+    tw[0] = next_tile(sps, nsp, own, 0, -1, q0, tree);
 #pragma unroll
-      for (int i = 0; i < kBuf - 1; ++i) {
-        ahead[i] = after(t, sps, nsp, own, q0, tree);
-        t = ahead[i];
-      }
-    }
+    for (int i = 1; i < kBuf; ++i) tw[i] = after(tw[i - 1], sps, nsp, own, q0, tree);
     auto issue = [&](const Tile& t, int buf) {
       const bool cc = t.sp < own;
       issue_tile<NW>(cc ? kc0p : k0p, t.k0, t.n, rs_kv, lds0 + oK + buf * kTileB, w, lane, vo_full);
       issue_tile<NW>(cc ? vc0p : v0p, t.k0, t.n, rs_kv, lds0 + oV_ + buf * kTileB, w, lane, vo_full);
     };
-    if (cur.valid) issue(cur, 0);
 #pragma unroll
-    for (int i = 0; i < kBuf - 2; ++i)
-      if (ahead[i].valid) issue(ahead[i], i + 1);
+    for (int i = 0; i < kBuf - 1; ++i)
+      if (i < kBuf - S && tw[i].valid) issue(tw[i], i);
     f32x4 O[HPW][8];
     float m[HPW];
     f32x4 L[HPW];  // row sums of the weights, formed on the matrix cores (every element the query's sum)
@@ -299,18 +299,21 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
       m[j] = -INFINITY;
       L[j] = zero;
     }
-    const bool active = 16 * wq < nq;
-    for (int it = 0; cur.valid; ++it) {
-      // this tile's copies (every wave's) have landed, and every wave is done
-      // with the buffer the next copy goes to (the previous tile's)
+    const bool active = 16 * qb < nq;
+    for (int g = 0; tw[0].valid; g += S) {
+      // the step's tiles have landed (every wave's copies), and every wave is
+      // done with the buffers the next copies go to (the previous step's)
       int pending = 0;
 #pragma unroll
-      for (int i = 0; i < kBuf - 2; ++i) pending += ahead[i].valid;
+      for (int i = 1; i < kBuf - 1; ++i) pending += (i >= S && i < kBuf - S) ? tw[i].valid : 0;
       wait_tiles<kPer>(pending);
       lds_barrier();
-      const int b = it & (kBuf - 1);
-      if (ahead[kBuf - 2].valid) issue(ahead[kBuf - 2], (it + kBuf - 1) & (kBuf - 1));
-      if (active) {
+#pragma unroll
+      for (int i = 1; i < kBuf; ++i)
+        if (i >= kBuf - S && tw[i].valid) issue(tw[i], (g + i) & (kBuf - 1));
+      const Tile cur = par ? tw[1] : tw[0];
+      const int b = (g + par) & (kBuf - 1);
+      if (active && cur.valid) {
         const unsigned char* kt = smem + oK + b * kTileB;
         const unsigned char* vt = smem + oV_ + b * kTileB;
         // S^T = K Q^T: lane (query l16, g4) holds keys 16 kb + 4 g4 + r
@@ -406,12 +409,58 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
           }
         }
       }
-      cur = ahead[0];
+      if (S == 2) {
 #pragma unroll
-      for (int i = 0; i < kBuf - 2; ++i) ahead[i] = ahead[i + 1];
-      ahead[kBuf - 2] = after(ahead[kBuf - 2], sps, nsp, own, q0, tree);
+        for (int i = 0; i < kBuf - 2; ++i) tw[i] = tw[i + 2];
+        tw[kBuf - 2] = after(tw[kBuf - 3], sps, nsp, own, q0, tree);
+        tw[kBuf - 1] = after(tw[kBuf - 2], sps, nsp, own, q0, tree);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kBuf - 1; ++i) tw[i] = tw[i + 1];
+        tw[kBuf - 1] = after(tw[kBuf - 2], sps, nsp, own, q0, tree);
+      }
     }
-    if (active && qi < nq) {
+    if (S == 2) {
+      // the odd-tile waves' states (references m, row sums L, unnormalised O)
+      // to their partners, through the idle tile ring: unit u of lane l of
+      // pair (head pair, query block) at ((pair U + u) 64 + l) 16 bytes
+      constexpr int U = HPW * 9 + 1;
+      f32x4* xb = reinterpret_cast<f32x4*>(smem) + (size_t)(wh * 2 + qb) * U * 64 + lane;
+      lds_barrier();  // every wave is done with the ring
+      if (par && active) {
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) xb[(j * 9 + dt) * 64] = O[j][dt];
+          xb[(j * 9 + 8) * 64] = L[j];
+        }
+        f32x4 mm = zero;
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) mm[j] = m[j];
+        xb[(HPW * 9) * 64] = mm;
+      }
+      lds_barrier();
+      if (!par && active) {
+        const f32x4 mm = xb[(HPW * 9) * 64];
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          // both sides rescaled to the larger reference (a side without keys has m = -inf and weight 0)
+          const float mo = mm[j], mx = fmaxf(m[j], mo);
+          const float fa = m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[j] - mx);
+          const float fb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mx);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            const f32x4 ob = xb[(j * 9 + dt) * 64];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[j][dt][r] = O[j][dt][r] * fa + ob[r] * fb;
+          }
+          const f32x4 lb = xb[(j * 9 + 8) * 64];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) L[j][r] = L[j][r] * fa + lb[r] * fb;
+        }
+      }
+    }
+    if (active && !par && qi < nq) {
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
         const float inv = 1.f / L[j][0];
