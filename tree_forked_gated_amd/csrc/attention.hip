@@ -233,7 +233,9 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
     lds_barrier();  // (also: every wave is done with the previous item's spans and tiles)
     const long long idx = s_claim;
     if (idx >= total) break;
-    const int item = (int)(idx / HG), hg0 = (int)(idx % HG) * kHW, h0 = hg0 + wh * HPW;
+    // items in reverse stream order: a segment's later chunks see more keys,
+    // so the longer items tend to go first and the short ones fill the tail
+    const int item = n_items - 1 - (int)(idx / HG), hg0 = (int)(idx % HG) * kHW, h0 = hg0 + wh * HPW;
     const int hk = hg0 / G;  // the item's heads share one key/value head (G is a multiple of kHW)
     const int4 inf = a.item_info[item];
     const int q0 = rfl(inf.x), nq = rfl(inf.y), tree = rfl(inf.z & 1), sq = rfl(inf.z >> 1);
