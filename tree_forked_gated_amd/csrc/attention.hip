@@ -248,12 +248,14 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
     }
     const int nsp = rfl(min(inf.w, kMaxLevels)) + own;
     if (tid >= own && tid < nsp) sps[tid] = a.spans[(size_t)item * a.max_levels + tid - own];
-    // A chunk of at most 32 queries on eight waves is split by key tiles: the
-    // waves of query blocks 2 and 3 take the odd tiles of blocks 0 and 1's
-    // queries (two tiles per step), and hand their softmax states over at the end.
-    const int S = (NW == 8 && nq <= 32) ? 2 : 1;  // tiles per step
-    const int par = S == 2 ? wq >> 1 : 0;          // the wave's tile within a step
-    const int qb = S == 2 ? wq & 1 : wq;           // the wave's query block
+    // Eight waves take two tiles per step (one barrier and one wait per 128
+    // keys). A chunk of at most 32 queries is split by key tiles: the waves of
+    // query blocks 2 and 3 take the odd tiles of blocks 0 and 1's queries, and
+    // hand their softmax states over at the end; otherwise every wave takes both.
+    const int S = NW == 8 ? 2 : 1;                 // tiles per step
+    const bool split = NW == 8 && nq <= 32;
+    const int par = split ? wq >> 1 : 0;           // the wave's tile within a step, when split
+    const int qb = split ? wq & 1 : wq;            // the wave's query block
     // this wave's 16 queries of each head as MFMA fragments (zero past the chunk's queries)
     const int qi = 16 * qb + l16;  // query within the chunk
     bf16x8 Qf[HPW][4];
@@ -313,8 +315,10 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
 #pragma unroll
       for (int i = 1; i < kBuf; ++i)
         if (i >= kBuf - S && tw[i].valid) issue(tw[i], (g + i) & (kBuf - 1));
-      const Tile cur = par ? tw[1] : tw[0];
-      const int b = (g + par) & (kBuf - 1);
+#pragma nounroll
+      for (int p = split ? par : 0; p < (split ? par + 1 : S); ++p) {
+      const Tile cur = p ? tw[1] : tw[0];
+      const int b = (g + p) & (kBuf - 1);
       if (active && cur.valid) {
         const unsigned char* kt = smem + oK + b * kTileB;
         const unsigned char* vt = smem + oV_ + b * kTileB;
@@ -411,6 +415,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
           }
         }
       }
+      }
       if (S == 2) {
 #pragma unroll
         for (int i = 0; i < kBuf - 2; ++i) tw[i] = tw[i + 2];
@@ -422,7 +427,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
         tw[kBuf - 1] = after(tw[kBuf - 2], sps, nsp, own, q0, tree);
       }
     }
-    if (S == 2) {
+    if (split) {
       // the odd-tile waves' states (references m, row sums L, unnormalised O)
       // to their partners, through the idle tile ring: unit u of lane l of
       // pair (head pair, query block) at ((pair U + u) 64 + l) 16 bytes
