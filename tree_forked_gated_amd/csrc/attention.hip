@@ -315,8 +315,9 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
 #pragma unroll
       for (int i = 1; i < kBuf; ++i)
         if (i >= kBuf - S && tw[i].valid) issue(tw[i], (g + i) & (kBuf - 1));
-#pragma nounroll
-      for (int p = split ? par : 0; p < (split ? par + 1 : S); ++p) {
+#pragma unroll
+      for (int p = 0; p < S; ++p) {  // unrolled: one tile's scores can overlap the other's softmax
+      if (split && p != par) continue;
       const Tile cur = p ? tw[1] : tw[0];
       const int b = (g + p) & (kBuf - 1);
       if (active && cur.valid) {
