@@ -151,6 +151,9 @@ def main():
     ap.add_argument("--attention", action="store_true",
                     help="time ForkAttention (gdn_tree_attention) over the workload's structure instead of the "
                          "recurrence: 16 query heads over 2 key/value heads, d 128, bf16")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the short runs of ForkAttention (decision-round structure) and chain rounds whose "
+                         "results the headline line carries under next_rows")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -159,9 +162,11 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr, flush=True)
         sys.exit(2)
     if args.attention:
-        return attention_main(args)
+        print(json.dumps(attention_main(args)), flush=True)
+        return
     if args.chain:
-        return chain_main(args)
+        print(json.dumps(chain_main(args)), flush=True)
+        return
 
     import torch
     from tree_forked_gated_amd import binding as B
@@ -457,7 +462,29 @@ def main():
         line["graph_replay"] = graph
     if mfma_probe is not None:
         line["mfma_probe"] = mfma_probe
+    if not args.no_next_rows:
+        line["next_rows"] = next_rows()
     print(json.dumps(line), flush=True)
+
+
+def next_rows():
+    """Short runs of the other measured paths (no CPU baselines): ForkAttention
+    over the decision-round structure and speculative chain rounds. Each entry
+    is that mode's own bench line, condensed; a failure is reported, not raised."""
+    out = {}
+    for name, fn, kw in [("fork_attention", attention_main, {"workload": "decision_round"}),
+                         ("chain_rounds", chain_main, {})]:
+        ns = argparse.Namespace(workload=kw.get("workload", "mixed_forest"), steps=10, warmup=2, rotate=1,
+                                no_cpu_baseline=True, cpu_min_s=0.0, cpu_threads=0)
+        try:
+            r = fn(ns)
+            out[name] = {"metric": r["metric"], "value": r["value"], "unit": r["unit"],
+                         "ms_per_step": r["ms_per_step"], "config": r["config"], "roofline": r["roofline"]}
+            if "other_mode" in r:
+                out[name]["other_mode"] = r["other_mode"]
+        except Exception as e:  # reported in the line; the headline stands on its own
+            out[name] = {"error": f"{type(e).__name__}: {e}"[:300]}
+    return out
 
 
 # ------------------------------------------------------------------ attention
@@ -583,7 +610,7 @@ def attention_main(args):
             "step_ms_percentiles": {"p10": round(float(np.percentile(per, 10)), 5),
                                     "p50": round(float(np.median(per)), 5),
                                     "p90": round(float(np.percentile(per, 90)), 5)}}
-    print(json.dumps(line), flush=True)
+    return line
 
 
 # --------------------------------------------------------------- chain rounds
@@ -689,7 +716,7 @@ def chain_main(args):
             "step_ms_percentiles": {"p10": round(float(np.percentile(d["per"], 10)), 5),
                                     "p50": round(float(np.median(d["per"])), 5),
                                     "p90": round(float(np.percentile(d["per"], 90)), 5)}}
-    print(json.dumps(line), flush=True)
+    return line
 
 
 if __name__ == "__main__":
