@@ -144,8 +144,10 @@ __global__ void __launch_bounds__(kThr) k_chain_step(const ChainArgs a) {
   const bool row_ok = r < rows;
   const int v0 = vb * kRows;
   if (s == 0 && h == 0 && vb == 0) check_all(a);
+  // The accepted count and the history length are checked only after the loads
+  // that do not depend on them (checkpoint rows, draft) have been issued, so
+  // that their round trip overlaps those loads.
   const int acc = a.accepted[s], hl = a.hist_len_in[s];
-  if (acc < 0 || acc > N || hl < 0 || hl > a.cap) return;  // reported by check_all
   const size_t SS = (size_t)Dv * DK;
   E* hk = reinterpret_cast<E*>(a.hist_k);
 
@@ -193,6 +195,7 @@ __global__ void __launch_bounds__(kThr) k_chain_step(const ChainArgs a) {
       dB[t] = upc<E>(bg[((size_t)s * N + t) * H + h]);
     }
   }
+  if (acc < 0 || acc > N || hl < 0 || hl > a.cap) return;  // reported by check_all
   // commit (Eq. 3) over the path: history slots [0, hl), then draft tokens [0, acc),
   // tiles of 16 tokens from the path's end
   const int L = hl + acc;
