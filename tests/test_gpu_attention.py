@@ -7,7 +7,7 @@ per-row bound of 5e-2 of the typical row norm. Cases: sequences of 1, 63, 64,
 65, 127, 128 and 129 tokens (tile boundaries), an empty sequence, forks from
 the last and first token of a tile and from mid-tile tokens, nested forks, draft
 trees (tree chunks), grouped key/value heads; at full size the decision-round
-structure with sampled rows; bitwise request isolation; plan reuse; the level
+structure and the mixed forest with sampled rows; bitwise request isolation; plan reuse; the level
 capacity error.
 """
 import numpy as np
@@ -121,6 +121,25 @@ def test_decision_round_full_size_sampled_rows():
     rows = np.unique(np.concatenate([wl.out_rows[::4], rng.integers(0, T, 48), [0, 8191, 8192, T - 1]]))
     ref = fork_attention(q, k, v, parent, seq, 128 ** -0.5, rows=rows)
     _compare("decision_round_sampled", out.float().cpu().numpy()[rows], ref)
+
+
+def test_mixed_forest_full_size_sampled_rows():
+    """The 65,536-token mixed forest at full size (nested forests of up to three
+    levels, trunks of 512-4096 tokens, 16 query heads over 2 key/value heads):
+    the oracle computes sampled rows one by one, among them every branch's first
+    token (its keys span the parent's prefix up to the fork) and the last token
+    of every forest."""
+    wl = W.mixed_forest(H=1, D=16)  # structure only
+    parent, seq = wl.parent, wl.seq_start
+    T = parent.shape[0]
+    rng = np.random.default_rng(17)
+    q, k, v = _values(rng, T, 16, 2)
+    say(f"attention mixed forest: T={T} sequences={seq.shape[0] - 1}")
+    out, _ = _run(parent, seq, q, k, v, 128 ** -0.5)
+    starts = np.nonzero((parent >= 0) & (parent != np.arange(T) - 1))[0]
+    rows = np.unique(np.concatenate([starts[::3], seq[1:] - 1, rng.integers(0, T, 48)]))
+    ref = fork_attention(q, k, v, parent, seq, 128 ** -0.5, rows=rows)
+    _compare("mixed_forest_sampled", out.float().cpu().numpy()[rows], ref)
 
 
 def _bits(t):

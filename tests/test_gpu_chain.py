@@ -31,15 +31,31 @@ def _draft(rng, n_seq, N, H, D, dtype):
 @pytest.mark.parametrize("dtype,D,cap", [("bf16", 128, 0), ("bf16", 128, 6), ("bf16", 128, 64), ("f32", 32, 5),
                                          ("f32", 64, 0)])
 def test_chain_rounds_against_oracle(dtype, D, cap):
+    _rounds_against_oracle(dtype, D, cap, n_seq=5, N=4, H=3, R=8, seed=100 + cap + D, tag="")
+
+
+@pytest.mark.parametrize("cap", [0, 16])
+def test_chain_rounds_full_size(cap):
+    """The benched size: 64 sequences x 32 heads x d 128, 4-token drafts, bf16,
+    with the state written every round (capacity 0) and with the 16-token
+    deferred history; three rounds and the forced flush, every sequence and
+    head against the oracle."""
+    _rounds_against_oracle("bf16", 128, cap, n_seq=64, N=4, H=32, R=3, seed=300 + cap, tag="full_")
+
+
+def _rounds_against_oracle(dtype, D, cap, n_seq, N, H, R, seed, tag):
     from tree_forked_gated_amd import binding as B
-    rng = np.random.default_rng(100 + cap + D)
-    n_seq, N, H, R = 5, 4, 3, 8
+    rng = np.random.default_rng(seed)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     S0 = W._init(rng, n_seq, H, D, D, True)
     rounds = [_draft(rng, n_seq, N, H, D, dtype) for _ in range(R)]
     acc = [rng.integers(0, N + 1, n_seq) for _ in range(R)]
-    acc[2][:] = 0
-    acc[3][:] = N
+    if R >= 4:  # a round that accepts nothing and one that accepts every draft
+        acc[2][:] = 0
+        acc[3][:] = N
+    else:  # half the sequences accept nothing in one round, the other half everything in the next
+        acc[R - 2][: n_seq // 2] = 0
+        acc[R - 1][n_seq // 2:] = N
     # accepted[r] is what the sampler keeps of draft r; round r + 1 commits it
     ref, S_end = chain_rounds(S0, rounds, acc)
     cr = B.ChainRounds(torch.from_numpy(S0).cuda(), N, cap, tdt, keep_state=True)
@@ -64,7 +80,7 @@ def test_chain_rounds_against_oracle(dtype, D, cap):
     # the forced flush leaves the committed state in the checkpoint and an empty history
     ck = rel_l2(cr.ckpt.cpu().numpy(), S_end)
     say(f"  worst rel-L2 over the rounds {worst}; checkpoint after the flush {ck:.2e}")
-    record_margin(f"chain/{dtype}_d{D}_cap{cap}", tol=tol, checkpoint=ck, **worst)
+    record_margin(f"chain/{tag}{dtype}_d{D}_cap{cap}", tol=tol, checkpoint=ck, **worst)
     assert ck <= tol
     assert int(cr.hist_len[1 - cr.cur].abs().sum()) == 0
 
