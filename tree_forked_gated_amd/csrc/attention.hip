@@ -21,14 +21,18 @@
 // planning workgroup, after the recurrence's metadata kernels), so launch
 // shapes depend only on the sizes.
 //
-// The attention kernel is a persistent grid of 4-wave workgroups that claim
-// (chunk, query heads) items: two query heads of one key/value group per item
-// when the group has an even number of them, so that every K and V fragment
-// read from LDS feeds two matrix products. Each wave owns 16 queries and walks
-// the item's key tiles of 64 keys with an online softmax: S^T = K Q^T and
-// O^T += V^T P^T on 16x16x32 bf16 matrix cores, fp32 softmax state. K and V
-// tiles are copied straight from HBM into LDS one tile ahead
-// (double-buffered). Fully visible tiles take no mask.
+// The attention kernel is a persistent grid of workgroups that claim (chunk,
+// query heads) items, last chunks first. Every wave holds 16 queries of two
+// query heads of one key/value group, so that every K and V fragment read from
+// LDS feeds two matrix products, and walks the item's key tiles of 64 keys with
+// an online softmax: S^T = K Q^T and O^T += V^T P^T on 16x16x32 bf16 matrix
+// cores, fp32 softmax state. When a key/value group has a multiple of four
+// query heads, a workgroup has eight waves (four query blocks x two head
+// pairs), a ring of four K/V tiles and two tiles per step (one barrier per 128
+// keys); a chunk of at most 32 queries is then split by key tiles over the
+// wave pairs. Otherwise four waves share a double-buffered pair of tiles. K and
+// V tiles are copied straight from HBM into LDS; fully visible tiles take no
+// mask.
 #include "gdn_internal.h"
 
 namespace gdn {
