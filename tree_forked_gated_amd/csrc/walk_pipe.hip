@@ -490,9 +490,16 @@ __device__ __forceinline__ void consume(const Touch& t) { asm volatile("" ::"v"(
 // it takes fewer copies). Measured on the chain walk: 2 blocks 2% faster than 4,
 // 0, 6 or 8.
 constexpr int kQSplit = 2;
+// With tiles of 16 or 32 columns the helpers set the pace of a chunk while the
+// state waves wait at the barrier, so there the state waves copy the K rows of
+// the chunk two ahead themselves (state_loop, from chunk 2 on) and helper 0
+// copies only its Q rows.
+template <int BV>
+constexpr bool kStateCopiesK = Cfg<BV>::NB == 1;
+template <bool WITH_K = true>
 __device__ __forceinline__ void issue_kq(const Args& a, const Desc& d, unsigned char* kq, int hid, int lane) {
   if (hid == 0) {
-    issue_rows<0, 16>(a, d, a.k, kq, lane);
+    if (WITH_K) issue_rows<0, 16>(a, d, a.k, kq, lane);
     issue_rows<0, kQSplit>(a, d, a.q, kq + 16384, lane);
   } else {
     issue_rows<kQSplit, 16>(a, d, a.q, kq + 16384, lane);
@@ -737,7 +744,16 @@ __device__ __forceinline__ void helper_loop(const Args& a, unsigned char* smem, 
     const Desc nd = uniform_desc(nds[it & 1]);                              // chunk it + 2: K, Q, tables
     const Desc nx = uniform_desc(*reinterpret_cast<const Desc*>(tb1 + tD));  // chunk it + 1: V, products
     if (hid == 1) tr = load_tokens(a, nd, lane);
-    if (nd.valid) issue_kq(a, nd, smem + C::oKQ + s2 * 32768, hid, lane);
+    // (the state waves copy K rows from their first chunk on, for chunk 2; chunk
+    // 1's are copied here, in iteration -1)
+    if (nd.valid) {
+      if constexpr (kStateCopiesK<BV>) {
+        if (it < 0) issue_kq<true>(a, nd, smem + C::oKQ + s2 * 32768, hid, lane);
+        else issue_kq<false>(a, nd, smem + C::oKQ + s2 * 32768, hid, lane);
+      } else {
+        issue_kq(a, nd, smem + C::oKQ + s2 * 32768, hid, lane);
+      }
+    }
     if (hid == 1 && nx.valid) issue_v<BV>(a, nx, smem + C::oV + ((it + 1) & 1) * C::VT, lane);
     Touch touch = {0u, 0u};
     if (nx.valid && nx.first && nx.sin) touch = prefetch_entry<BV>(nx.sin, hid, lane);
@@ -1156,17 +1172,37 @@ __device__ __forceinline__ void state_loop(const Args& a, unsigned char* smem, i
     const unsigned char* pr = smem + C::oPR + (it & 1) * kPR;
     const int v0w = v0 + 16 * NB * ws;  // first column of the wave
 
+    if constexpr (kStateCopiesK<BV>) {
+      // The entry state loaded before the barrier is awaited here, by a wait
+      // the compiler's own wait insertion sees: the copies below are inline
+      // assembly, invisible to it, and a wait it placed later for the state
+      // would wait for them too.
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
+    }
     if (first) {  // a new item: its entry state, loaded before the barrier
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int m = 0; m < 4; ++m) Sb[nb][m] = cat8b(to_bf4(ST[nb][2 * m]), to_bf4(ST[nb][2 * m + 1]));
     }
+    if constexpr (kStateCopiesK<BV>) {  // K rows of chunk it + 2, split over the state waves
+      const Desc nd = uniform_desc(reinterpret_cast<const Desc*>(smem + C::oND)[it & 1]);
+      if (nd.valid) {
+        unsigned char* k2 = smem + C::oKQ + ((it + 2) % 3) * 32768;
+        if constexpr (C::NS == 1) {
+          issue_rows<0, 16>(a, nd, a.k, k2, lane);
+        } else {
+          if (ws == 0) issue_rows<0, 8>(a, nd, a.k, k2, lane);
+          else issue_rows<8, 16>(a, nd, a.k, k2, lane);
+        }
+      }
+    }
     if (has_out)
       state_chunk<BV, true>(a, smem, tb, kq, vt, pr, o, ST, Sb, it, t0, n, h, v0w, mode, need_exit, todo, lane);
     else
       state_chunk<BV, false>(a, smem, tb, kq, vt, pr, o, ST, Sb, it, t0, n, h, v0w, mode, need_exit, todo, lane);
     WALK_STAMP(it, 7);
+    if constexpr (kStateCopiesK<BV>) wait_vm();  // this wave's copies have landed (before the next entry loads)
     const Desc* dn = reinterpret_cast<const Desc*>(smem + C::oTB + ((it + 1) % 3) * kTB + tD);
     cd = load_sdesc(reinterpret_cast<const unsigned char*>(dn));
     WALK_STAMP(it, 8);
