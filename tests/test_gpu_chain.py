@@ -2,7 +2,8 @@
 against the speculative chain-round oracle (oracle/chain.py).
 
 Eight rounds of chain drafts per sequence, with seeded accepted counts
-(including rounds that accept nothing and rounds that accept the whole draft).
+(including rounds that accept nothing and rounds that accept the whole draft),
+with drafts of 4 tokens and of 12.
 Every round's outputs and pseudo-values, and the committed state it starts from
 (state_out), are compared with the oracle: with the state written every round
 (history capacity 0), with a short history that flushes every few rounds, and
@@ -32,6 +33,13 @@ def _draft(rng, n_seq, N, H, D, dtype):
                                          ("f32", 64, 0)])
 def test_chain_rounds_against_oracle(dtype, D, cap):
     _rounds_against_oracle(dtype, D, cap, n_seq=5, N=4, H=3, R=8, seed=100 + cap + D, tag="")
+
+
+@pytest.mark.parametrize("dtype,D,cap", [("bf16", 128, 0), ("bf16", 128, 30), ("f32", 64, 13)])
+def test_chain_rounds_long_drafts(dtype, D, cap):
+    """Drafts of 12 tokens (three times the benched length), with histories
+    that flush every few rounds (30, 13) or never hold anything (0)."""
+    _rounds_against_oracle(dtype, D, cap, n_seq=4, N=12, H=2, R=5, seed=200 + cap + D, tag="n12_")
 
 
 @pytest.mark.parametrize("cap", [0, 16])
