@@ -91,15 +91,23 @@ def commit_counts(wl):
 
 # -------------------------------------------------------------------- traffic
 
+def _code_only(text):
+    """Source text without // comments and blank lines, each line stripped:
+    what the compiler sees of it (the walk's sources hold no // inside a
+    string and no block comments)."""
+    lines = (ln.split("//", 1)[0].strip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_digest():
-    """Digest of what defines the walk kernel's code: its sources and the
-    compiler flags it is built with (its traffic does not depend on the
-    metadata or commit kernels)."""
+    """Digest of what defines the walk kernel's code: its sources without
+    their comments and the compiler flags it is built with (its traffic does
+    not depend on the metadata or commit kernels, nor on a comment)."""
     from tree_forked_gated_amd import build as hipbuild
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "tree_forked_gated_amd")
     for name in ("csrc/gdn_internal.h", "csrc/walk_pipe.hip"):
-        h.update(open(os.path.join(pkg, name), "rb").read())
+        h.update(_code_only(open(os.path.join(pkg, name)).read()).encode())
     flags = [f for f in hipbuild.FLAGS if not f.startswith(ROOT)] + hipbuild.FILE_FLAGS.get("walk_pipe.hip", [])
     h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]

@@ -28,9 +28,10 @@
 // * two helper waves work one chunk ahead: from that chunk's K and Q they form
 //   the A tiles, the inverses of the diagonal blocks and the masked, decayed
 //   P = M . exp . Q K^T, and leave them in LDS as ready MFMA operands. They
-//   also copy q and k two chunks ahead and v one chunk ahead from HBM into LDS
-//   (direct-to-LDS loads); the first helper also walks the item list and the
-//   second prepares each chunk's token tables.
+//   also copy q two chunks ahead and v one chunk ahead from HBM into LDS
+//   (direct-to-LDS loads), and k two chunks ahead in a tile of 64 columns (in
+//   narrower tiles the state waves copy k); the first helper also walks the
+//   item list and the second prepares each chunk's token tables.
 //
 // One barrier per chunk separates the stages. The state is kept transposed in
 // the MFMA accumulator layout, with its d_k index permuted so that the
@@ -485,10 +486,10 @@ __device__ __forceinline__ Touch prefetch_entry(const float* sin, int hid, int l
 }
 __device__ __forceinline__ void consume(const Touch& t) { asm volatile("" ::"v"(t.w0), "v"(t.w1)); }
 
-// Helper 0 copies K and the first kQSplit blocks of 4 rows of Q, helper 1 the
-// rest of Q (helper 0 also inverts the diagonal blocks and feeds the items, so
-// it takes fewer copies). Measured on the chain walk: 2 blocks 2% faster than 4,
-// 0, 6 or 8.
+// Helper 0 copies K (tiles of 64 columns) and the first kQSplit blocks of 4 rows
+// of Q, helper 1 the rest of Q (helper 0 also inverts the diagonal blocks and
+// feeds the items, so it takes fewer copies). Measured on the chain walk while
+// helper 0 also copied K there: 2 blocks 2% faster than 4, 0, 6 or 8.
 constexpr int kQSplit = 2;
 // With tiles of 16 or 32 columns the helpers set the pace of a chunk while the
 // state waves wait at the barrier, so there the state waves copy the K rows of
