@@ -50,3 +50,14 @@ def test_tree_and_chain_tokens_split_by_sequence_length():
                     np.zeros(0, dtype=np.int32))
     c = bench.algorithmic_counts(wl, n_out=129, n_state=0, keep_pseudo=False)
     assert c["flops"] == H * (64 * (10 * 64 * d + 4 * d * d) + 65 * (10 * 64 * d + 6 * d * d))
+
+
+def test_walk_digest_ignores_comments_only():
+    """The traffic counters are keyed by the walk's code: a comment or a blank
+    line leaves the key alone, a changed statement does not."""
+    import bench
+    src = "int a = 1;  // one\n\n// a note\n  int b = a + 2;\n"
+    assert bench._code_only(src) == "int a = 1;\nint b = a + 2;"
+    assert bench._code_only(src.replace("// a note", "// another note\n\n")) == bench._code_only(src)
+    assert bench._code_only(src.replace("a + 2", "a + 3")) != bench._code_only(src)
+    assert len(bench.source_digest()) == 16
