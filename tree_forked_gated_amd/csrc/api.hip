@@ -1,6 +1,8 @@
 // The C ABI of include/gdn_tree.h: argument checks on the host, then kernel
-// launches on the caller's stream. No allocation, no synchronisation (except
-// gdn_tree_check_error), no state kept between calls.
+// launches on the caller's stream. No allocation and no synchronisation
+// (except gdn_tree_check_error). Between calls the library keeps only
+// per-device caches of the CU count and of kernel attributes, and the static
+// workspace of gdn_tree_forward_static (whose contents a call rebuilds).
 #include <stdio.h>
 
 #include <atomic>
