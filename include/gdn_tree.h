@@ -39,9 +39,10 @@
  *    from parent_idx on every replay.
  *  - The caller owns every buffer, the workspace included, and keeps them
  *    alive until the stream has passed the call. The library allocates no
- *    device memory and keeps no mutable global state besides a thread-local
- *    text for the last host error. Calls on different streams with different
- *    workspaces may overlap.
+ *    device memory. Its global state is a thread-local text for the last host
+ *    error, per-device caches of the CU count and kernel attributes, and the
+ *    static workspace of gdn_tree_forward_static (below). Calls on different
+ *    streams with different workspaces may overlap.
  *  - Return value: GDN_OK or a negative gdn_status found synchronously on the
  *    host (nothing is enqueued then). Structural problems of the tree are
  *    found on the device: the kernels record the smallest (code, index) in the
