@@ -242,6 +242,12 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
     const int item = n_items - 1 - (int)(idx / HG), hg0 = (int)(idx % HG) * kHW, h0 = hg0 + wh * HPW;
     const int hk = hg0 / G;  // the item's heads share one key/value head (G is a multiple of kHW)
     const int4 inf = a.item_info[item];
+    // Every span slot of the item is read together with its record (the table
+    // holds max_levels slots per item), so the list does not wait for the
+    // record's span count; only the item's own spans reach LDS below.
+    const int span_slots = min(a.max_levels, kMaxLevels);
+    int2 spv = make_int2(0, 0);
+    if (tid < span_slots) spv = a.spans[(size_t)item * a.max_levels + tid];
     const int q0 = rfl(inf.x), nq = rfl(inf.y), tree = rfl(inf.z & 1), sq = rfl(inf.z >> 1);
     // the sequence's cached keys, if any, come first (span 0), then the item's spans
     int own = 0;
@@ -251,7 +257,7 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) k_fork_attn(const At
       if (own && tid == 0) sps[0] = make_int2(c0, c1 - 1);
     }
     const int nsp = rfl(min(inf.w, kMaxLevels)) + own;
-    if (tid >= own && tid < nsp) sps[tid] = a.spans[(size_t)item * a.max_levels + tid - own];
+    if (tid < span_slots && tid + own < nsp) sps[tid + own] = spv;
     // Eight waves take two tiles per step (one barrier and one wait per 128
     // keys). A chunk of at most 32 queries is split by key tiles: the waves of
     // query blocks 2 and 3 take the odd tiles of blocks 0 and 1's queries, and
