@@ -189,12 +189,14 @@ typedef struct gdn_tree_fwd_args {
  *                       indices from a root (parent -1) down to the accepted node, each node
  *                       the parent of the next; an empty path commits the initial state.
  *                       path_nodes is required whenever n_path > 0 (any valid address when
- *                       every path is empty). Every node is checked against its sequence's
- *                       range inside [0, T) before anything indexed by it is read; a bad path
+ *                       every path is empty). A node's index is clamped into [0, T) before
+ *                       anything indexed by it is read, and every node is checked against its
+ *                       sequence's range and parent before any state is written; a bad path
  *                       raises GDN_DEV_PATH (the smallest such path) and its state is not written.
  *  path_seq [n_path]    sequence of each path
  *  out_state            [n_path, H, Dv, Dk] fp32
  *  workspace            device buffer of at least gdn_tree_commit_workspace_size() bytes
+ * k, pseudo_v, init_state and out_state must be 16-byte aligned (GDN_ERR_ARGS otherwise).
  */
 typedef struct gdn_tree_commit_args {
   gdn_tree_dims dims;

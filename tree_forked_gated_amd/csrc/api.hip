@@ -315,8 +315,9 @@ int gdn_tree_commit(const gdn_tree_commit_args* a, void* stream) {
       return fail(GDN_ERR_NULL,
                   "k, log_gate, parent_idx, seq_start, pseudo_v, path_ptr, path_nodes, path_seq and out_state are "
                   "required when n_path > 0");
-    if (!aligned16(a->out_state) || (a->init_state && !aligned16(a->init_state)))
-      return fail(GDN_ERR_ARGS, "states must be 16-byte aligned");
+    if (!aligned16(a->out_state) || (a->init_state && !aligned16(a->init_state)) || !aligned16(a->k) ||
+        !aligned16(a->pseudo_v))
+      return fail(GDN_ERR_ARGS, "states, k and pseudo_v must be 16-byte aligned");
   }
   hipError_t e = launch_commit(*a, (unsigned long long*)a->workspace, (hipStream_t)stream);
   if (e != hipSuccess) return fail_hip(e, "gdn_tree_commit");

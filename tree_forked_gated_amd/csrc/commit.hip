@@ -3,11 +3,17 @@
 //
 //   S_a = g_a S_0 + sum over i on the root path of a (a included) of (g_a / g_i) vt_i k_i^T
 //
-// g_a / g_i = exp(sum of the log gates strictly after i on the path), summed
-// from a backwards in fp32; g_a = exp of the whole path's sum. One workgroup
-// per (path, head, 32 rows of S): it reads S_0 once, the path's pseudo-values,
-// keys and gates, and writes S_a once. The kernel is bound by those two state
-// streams (HBM), so it stays on plain fp32 FMAs with float4 loads and stores.
+// g_a / g_i = exp(sum of the log gates strictly after i on the path) and g_a =
+// exp of the whole path's sum. The path is taken from its root in tiles of 16
+// nodes, so the sum is the same recurrence tile by tile:
+//
+//   S <- exp(sum of the tile's log gates) S + sum over i in the tile of exp(sum of its log gates after i) vt_i k_i^T
+//
+// starting from S_0, all in fp32. One workgroup per (path, head, 32 rows of S):
+// it reads S_0 once, the path's pseudo-values, keys and gates, and writes S_a
+// once. The kernel is bound by those two state streams (HBM), so it stays on
+// plain fp32 FMAs with 16-byte loads and stores, and holds the rows of S in one
+// set of registers (eight workgroups fit on a CU).
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -38,15 +44,16 @@ struct CommitArgs {
   int own_err;  // 1: workgroup (0, 0, 0) checks every path and stores the error word itself
 };
 
-template <typename E>
-__device__ inline float upc(E x) { return (float)x; }
+__device__ inline float upc(__bf16 x) { return (float)x; }
+__device__ inline float upc(float x) { return x; }
 
 __global__ void k_reset(unsigned long long* err) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *err = kNoError;
 }
 
 // Is path p a parent chain from a root of its sequence down to its last node?
-// Every index is checked before it is used.
+// Every index is checked before it is used; the nodes' loads do not wait for
+// the verdict on the nodes before them.
 __device__ inline bool path_ok(const CommitArgs& a, int p) {
   const int seq = a.path_seq[p];
   const int beg = a.path_ptr[p], end = a.path_ptr[p + 1];
@@ -54,12 +61,16 @@ __device__ inline bool path_ok(const CommitArgs& a, int p) {
   if (end == beg) return true;
   const int s_0 = a.seq_start[seq], s_1 = a.seq_start[seq + 1];
   if (s_0 < 0 || s_1 > a.T || s_1 <= s_0) return false;
+  bool ok = true;
+  int want = -1;
+#pragma unroll 4
   for (int j = beg; j < end; ++j) {
     const int t = a.path_nodes[j];
-    const int want = (j == beg) ? -1 : a.path_nodes[j - 1];
-    if (t < s_0 || t >= s_1 || a.parent[t] != want) return false;
+    const bool in = t >= s_0 && t < s_1;
+    ok &= in && a.parent[in ? t : s_0] == want;
+    want = t;
   }
-  return true;
+  return ok;
 }
 
 // The error word of a call with few paths: the smallest bad path, found by one
@@ -77,19 +88,20 @@ __device__ inline void check_all_paths(const CommitArgs& a) {
                                    : (((unsigned long long)(unsigned)GDN_DEV_PATH << 32) | (unsigned)s_first);
 }
 
-// One workgroup per (path, head, 32 rows of S). The rows of S_0 are loaded
-// first, so that they arrive while the path is summed. The path is staged in
-// LDS 16 nodes at a time, from the accepted node backwards: each node is
-// checked (in its sequence, parent = previous node) in the same pass that loads
-// its key, pseudo-values and gate, with the index held in range until the
-// check is decided, just before the stores.
+// One workgroup per (path, head, 32 rows of S). The rows of S_0 are requested
+// first, so that they arrive while the path is staged. The path is staged in
+// LDS 16 nodes at a time from its root: each node is checked (in its sequence,
+// parent = previous node) in the same pass that loads its key, pseudo-values
+// and gate. Until the check is decided, a node's index is clamped into [0, T)
+// for those loads, so that they need not wait for the sequence's range; the
+// verdict is taken before any store.
 template <typename E>
-__global__ void __launch_bounds__(kThreads, 6) k_commit(CommitArgs a) {
-  __shared__ float sK[kPathTile][128 + 4];
-  __shared__ float sV[kPathTile][kRows];
+__global__ void __launch_bounds__(kThreads, 8) k_commit(CommitArgs a) {
+  constexpr int kEPer = 16 / sizeof(E);  // key elements per 16-byte piece
+  __shared__ __attribute__((aligned(16))) float sK[kPathTile][128 + 4];
+  __shared__ __attribute__((aligned(16))) float sV[kPathTile][kRows];
   __shared__ float sG[kPathTile];
-  __shared__ float sW[kPathTile];
-  __shared__ float sSigma;
+  __shared__ float sW[kPathTile + 1];  // the nodes' weights, then the tile's decay
   const int p = blockIdx.x, h = blockIdx.y, vb = blockIdx.z;
   const int tid = threadIdx.x;
   const int Dk = a.Dk, H = a.H, Dv = a.Dv;
@@ -101,8 +113,8 @@ __global__ void __launch_bounds__(kThreads, 6) k_commit(CommitArgs a) {
   const int beg = a.path_ptr[p], end = a.path_ptr[p + 1];
   const bool bad_path = (seq < 0 || seq >= a.n_seq || end < beg);
   bool bad = bad_path;
-  // S_0 rows of this block (zeros without initial states)
-  float4 s0[kPer4];
+  // S starts as the S_0 rows of this block (zeros without initial states)
+  float4 acc[kPer4];
   const float* S0 = (!bad_path && a.init) ? a.init + ((size_t)seq * H + h) * SS : nullptr;
 #pragma unroll
   for (int i = 0; i < kPer4; ++i) {
@@ -110,89 +122,91 @@ __global__ void __launch_bounds__(kThreads, 6) k_commit(CommitArgs a) {
     const int r = gidx / per_row4, d = (gidx % per_row4) * 4;
     f32x4n v = {0.f, 0.f, 0.f, 0.f};
     if (S0 && gidx < n4 && r < rows) v = __builtin_nontemporal_load(reinterpret_cast<const f32x4n*>(S0 + (size_t)(vb * kRows + r) * Dk + d));
-    s0[i] = make_float4(v[0], v[1], v[2], v[3]);
+    acc[i] = make_float4(v[0], v[1], v[2], v[3]);
   }
   const E* kg = reinterpret_cast<const E*>(a.k);
   const E* gg = reinterpret_cast<const E*>(a.g);
-  int s_0 = bad_path ? 0 : a.seq_start[seq], s_1 = bad_path ? 0 : a.seq_start[seq + 1];
-  // a non-empty path needs a non-empty sequence inside [0, T); nothing is loaded otherwise
-  const bool no_tokens = !bad_path && end > beg && (s_1 <= s_0 || s_0 < 0 || s_1 > a.T);
-  if (no_tokens) s_0 = s_1 = 0;
-  bad |= no_tokens;
-  float4 acc[kPer4];
-#pragma unroll
-  for (int i = 0; i < kPer4; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (tid == 0) sSigma = 0.f;
-  __syncthreads();
-  for (int tile_end = (bad_path || no_tokens) ? beg : end; tile_end > beg; tile_end -= kPathTile) {
-    const int tile_beg = max(beg, tile_end - kPathTile);
-    const int nt = tile_end - tile_beg;
+  const int s_0 = bad_path ? 0 : a.seq_start[seq], s_1 = bad_path ? 0 : a.seq_start[seq + 1];
+  const int last = a.T - 1;  // a.T > 0 whenever a path has nodes that pass the check
+  const int kpieces = Dk / kEPer;  // 16-byte pieces of a key row
+  const int vpieces = rows / 4;    // float4 pieces of the block's pseudo-value rows
+  const int n_nodes = (bad_path || a.T <= 0) ? 0 : end - beg;
+  for (int tile_beg = beg; tile_beg < beg + n_nodes; tile_beg += kPathTile) {
+    const int nt = min(kPathTile, beg + n_nodes - tile_beg);
     if (tid < nt) {  // check the node and load its gate
       const int j = tile_beg + tid;
       const int t = a.path_nodes[j];
       const int want = (j == beg) ? -1 : a.path_nodes[j - 1];
-      const bool ok = t >= s_0 && t < s_1 && a.parent[t] == want;
-      bad |= !ok;
-      sG[tid] = ok ? upc<E>(gg[(size_t)t * H + h]) : 0.f;
+      const int tc = min(max(t, 0), last);
+      bad |= !(t >= s_0 && t < s_1 && a.parent[tc] == want);
+      sG[tid] = upc(gg[(size_t)tc * H + h]);
     }
-    for (int idx = tid; idx < nt * Dk; idx += kThreads) {
-      const int j = idx / Dk, d = idx % Dk;
-      int t = a.path_nodes[tile_beg + j];
-      t = (t >= s_0 && t < s_1) ? t : s_0;  // in range until the check is decided
-      sK[j][d] = upc<E>(kg[((size_t)t * H + h) * Dk + d]);
+    if (tid < nt * kpieces) {  // one 16-byte piece of a key row per thread
+      const int j = tid / kpieces, c = tid % kpieces;
+      const int tc = min(max(a.path_nodes[tile_beg + j], 0), last);
+      const uint4 raw = *reinterpret_cast<const uint4*>(kg + ((size_t)tc * H + h) * Dk + c * kEPer);
+      const E* e = reinterpret_cast<const E*>(&raw);
+#pragma unroll
+      for (int x = 0; x < kEPer; x += 4)
+        *reinterpret_cast<float4*>(&sK[j][c * kEPer + x]) = make_float4(upc(e[x]), upc(e[x + 1]), upc(e[x + 2]), upc(e[x + 3]));
     }
-    for (int idx = tid; idx < nt * kRows; idx += kThreads) {
-      const int j = idx / kRows, r = idx % kRows;
-      int t = a.path_nodes[tile_beg + j];
-      t = (t >= s_0 && t < s_1) ? t : s_0;
-      sV[j][r] = r < rows ? a.pv[((size_t)t * H + h) * Dv + vb * kRows + r] : 0.f;
+    if (tid < nt * (kRows / 4)) {  // one float4 of a pseudo-value row per thread
+      const int j = tid / (kRows / 4), c = tid % (kRows / 4);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c < vpieces) {
+        const int tc = min(max(a.path_nodes[tile_beg + j], 0), last);
+        v = *reinterpret_cast<const float4*>(a.pv + ((size_t)tc * H + h) * Dv + vb * kRows + 4 * c);
+      }
+      *reinterpret_cast<float4*>(&sV[j][4 * c]) = v;
     }
     __syncthreads();
-    if (tid == 0) {  // weights exp(sum of log gates after node j), accumulated from a backwards
-      float sigma = sSigma;
+    if (tid == 0) {  // weights exp(sum of the tile's log gates after node j), from the tile's end
+      float sigma = 0.f;
       for (int j = nt - 1; j >= 0; --j) {
         sW[j] = __expf(sigma);
         sigma += sG[j];
       }
-      sSigma = sigma;
+      sW[kPathTile] = __expf(sigma);
     }
     __syncthreads();
+    const float dec = sW[kPathTile];
 #pragma unroll
     for (int i = 0; i < kPer4; ++i) {
       const int gidx = tid + kThreads * i;
       if (gidx < n4) {
         const int r = gidx / per_row4, d = (gidx % per_row4) * 4;
         float4 s = acc[i];
-        for (int j = nt - 1; j >= 0; --j) {
+        s.x *= dec;
+        s.y *= dec;
+        s.z *= dec;
+        s.w *= dec;
+        for (int j = 0; j < nt; ++j) {
           const float wv = sW[j] * sV[j][r];
-          s.x += wv * sK[j][d];
-          s.y += wv * sK[j][d + 1];
-          s.z += wv * sK[j][d + 2];
-          s.w += wv * sK[j][d + 3];
+          const float4 kk = *reinterpret_cast<const float4*>(&sK[j][d]);
+          s.x += wv * kk.x;
+          s.y += wv * kk.y;
+          s.z += wv * kk.z;
+          s.w += wv * kk.w;
         }
         acc[i] = s;
       }
     }
     __syncthreads();
   }
+  // a non-empty path needs a non-empty sequence inside [0, T)
+  if (!bad_path && end > beg && (s_1 <= s_0 || s_0 < 0 || s_1 > a.T)) bad = true;
   if (a.own_err && p == 0 && h == 0 && vb == 0) check_all_paths(a);
   if (__syncthreads_or(bad)) {
     if (tid == 0 && !a.own_err) raise_error(a.err, GDN_DEV_PATH, p);
     return;
   }
-  const float ga = __expf(sSigma);
   float* dst = a.out + ((size_t)p * H + h) * SS;
 #pragma unroll
   for (int i = 0; i < kPer4; ++i) {
     const int gidx = tid + kThreads * i;
     const int r = gidx / per_row4, d = (gidx % per_row4) * 4;
     if (gidx < n4 && r < rows) {
-      float4 o = acc[i];
-      o.x += ga * s0[i].x;
-      o.y += ga * s0[i].y;
-      o.z += ga * s0[i].z;
-      o.w += ga * s0[i].w;
-      f32x4n ov = {o.x, o.y, o.z, o.w};
+      const f32x4n ov = {acc[i].x, acc[i].y, acc[i].z, acc[i].w};
       __builtin_nontemporal_store(ov, reinterpret_cast<f32x4n*>(dst + (size_t)(vb * kRows + r) * Dk + d));
     }
   }
