@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kRows = 32;   // rows of S (d_v) per workgroup
 constexpr int kThr = 256;   // 8 threads per row
-constexpr int kTileP = 32;  // path tokens staged in LDS at a time
+constexpr int kTileP = 16;  // path tokens staged in LDS at a time
 
 struct ChainArgs {
   float* ckpt;
@@ -129,13 +129,13 @@ __device__ inline void stage_path(const ChainArgs& a, int s, int h, int v0, int 
 }
 
 template <typename E, int DK>
-__global__ void __launch_bounds__(kThr) k_chain_step(const ChainArgs a) {
+__global__ void __launch_bounds__(kThr, 8) k_chain_step(const ChainArgs a) {
   constexpr int CPT = DK / 8;  // columns per thread
   constexpr int VE = Vec16<E>::n;
   __shared__ float sK[kTileP][DK + 4];
   __shared__ float sV[kTileP][kRows];
   __shared__ float sG[kTileP];
-  __shared__ float sW[kTileP];
+  __shared__ float sW[kTileP + 1];  // the tokens' weights, then the tile's decay
   extern __shared__ float dyn[];  // draft: k [N][DK], q [N][DK], v [N][kRows], gate [N], beta [N]
   const int s = blockIdx.x, h = blockIdx.y, vb = blockIdx.z;
   const int tid = threadIdx.x, r = tid >> 3, cq = tid & 7;
@@ -196,70 +196,60 @@ __global__ void __launch_bounds__(kThr) k_chain_step(const ChainArgs a) {
     }
   }
   if (acc < 0 || acc > N || hl < 0 || hl > a.cap) return;  // reported by check_all
-  // commit (Eq. 3) over the path: history slots [0, hl), then draft tokens [0, acc),
-  // tiles of 16 tokens from the path's end
+  // commit (Eq. 3) over the path: history slots [0, hl), then draft tokens [0, acc)
   const int L = hl + acc;
-  int tile_end = L;
-  int nt = min(kTileP, tile_end);
-  if (nt > 0) stage_path<E, DK>(a, s, h, v0, rows, hl, tile_end - nt, nt, sK, sV, sG);
-  __syncthreads();
-  float accum[CPT];
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) accum[i] = 0.f;
-  // the accepted tokens join the history (unless this round flushes), copied from the
-  // staged tile: they are its last acc tokens (acc <= N <= 32 = kTileP)
-  static_assert(kTileP >= 32, "the accepted prefix of a draft must fit one staged tile");
   const bool flush = a.flush || L > a.cap;
+  // the accepted tokens join the history (unless this round flushes), copied
+  // from the previous draft's pseudo-values, keys and gates
   if (!flush) {
-    const int j0 = L - nt;  // first path token of the staged tile
+    const E* pk = reinterpret_cast<const E*>(a.prev_k);
+    const E* pg = reinterpret_cast<const E*>(a.prev_g);
     for (int idx = tid; idx < acc * (kRows / 4); idx += kThr) {
       const int i = idx / (kRows / 4), c4 = idx % (kRows / 4);
       if (4 * c4 < rows)
         *reinterpret_cast<float4*>(a.hist_pv + (((size_t)s * a.cap + hl + i) * H + h) * Dv + v0 + 4 * c4) =
-            *reinterpret_cast<const float4*>(&sV[hl + i - j0][4 * c4]);
+            *reinterpret_cast<const float4*>(a.prev_pv + (((size_t)s * N + i) * H + h) * Dv + v0 + 4 * c4);
     }
     if (vb == 0) {
-      for (int idx = tid; idx < acc * DK; idx += kThr) {
-        const int i = idx / DK, d = idx % DK;
-        hk[(((size_t)s * a.cap + hl + i) * H + h) * DK + d] = (E)sK[hl + i - j0][d];
+      for (int idx = tid; idx < acc * (DK / VE); idx += kThr) {
+        const int i = idx / (DK / VE), part = idx % (DK / VE);
+        *reinterpret_cast<uint4*>(hk + (((size_t)s * a.cap + hl + i) * H + h) * DK + part * VE) =
+            *reinterpret_cast<const uint4*>(pk + (((size_t)s * N + i) * H + h) * DK + part * VE);
       }
-      if (tid < acc) a.hist_g[((size_t)s * a.cap + hl + tid) * H + h] = sG[hl + tid - j0];
+      if (tid < acc) a.hist_g[((size_t)s * a.cap + hl + tid) * H + h] = upc<E>(pg[((size_t)s * N + tid) * H + h]);
     }
   }
-  float carry = 0.f;  // sum of the log gates after the current tile
-  while (nt > 0) {
-    // weight of token jj: exp(sum of the log gates after it on the path), by a
-    // suffix scan over the first kTileP lanes (nt <= kTileP)
-    if (tid < 64) {
+  // The path is taken from its start in tiles of kTileP tokens, which regroups
+  // Eq. 3 tile by tile: S <- exp(sum of the tile's log gates) S + sum over the
+  // tile of exp(sum of its log gates after j) vt_j k_j^T, from the checkpoint.
+  for (int j0 = 0; j0 < L; j0 += kTileP) {
+    const int nt = min(kTileP, L - j0);
+    stage_path<E, DK>(a, s, h, v0, rows, hl, j0, nt, sK, sV, sG);
+    __syncthreads();
+    if (tid < 64) {  // inclusive suffix sums of the tile's log gates over the first kTileP lanes
       const float gv = tid < nt ? sG[tid] : 0.f;
-      float x = gv;  // inclusive suffix sum
+      float x = gv;
 #pragma unroll
       for (int o = 1; o < kTileP; o <<= 1) {
         const float y = __shfl_down(x, o);
         if (tid + o < kTileP) x += y;
       }
-      if (tid < nt) sW[tid] = __expf(carry + x - gv);
+      if (tid < nt) sW[tid] = __expf(x - gv);
+      if (tid == 0) sW[kTileP] = __expf(x);
     }
-    float tile_sum = 0.f;
-    for (int i = nt - 1; i >= 0; --i) tile_sum += sG[i];
     __syncthreads();
-    for (int jj = nt - 1; jj >= 0; --jj) {
+    const float dec = sW[kTileP];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) S[i] *= dec;
+    for (int jj = 0; jj < nt; ++jj) {
       const float wv = sW[jj] * sV[jj][r];
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) accum[i] += wv * sK[jj][4 * cq + 8 * (i & ~3) + (i & 3)];
+      for (int i = 0; i < CPT; ++i) S[i] += wv * sK[jj][4 * cq + 8 * (i & ~3) + (i & 3)];
     }
-    carry += tile_sum;
-    tile_end -= nt;
-    nt = min(kTileP, tile_end);
     __syncthreads();
-    if (nt > 0) {
-      stage_path<E, DK>(a, s, h, v0, rows, hl, tile_end - nt, nt, sK, sV, sG);
-      __syncthreads();
-    }
   }
-  const float gall = __expf(carry);
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) S[i] = gall * S[i] + accum[i];
+
+  __syncthreads();  // the draft in LDS is complete (an empty path runs no tile above)
 
   // flush the committed state (or keep the accepted tokens as history, above)
   float* stores[2] = {flush ? a.ckpt : nullptr, a.state_out};
