@@ -56,6 +56,27 @@ struct ChainArgs {
 template <typename E>
 __device__ inline float upc(E x) { return (float)x; }
 
+// Sum over the eight threads of a row (lanes 8 i .. 8 i + 7), the same value in
+// each: DPP lane moves (quad permutations for xor 1 and xor 2, then the mirror
+// within eight lanes), ALU operations instead of LDS permutes.
+__device__ __forceinline__ float row_sum8(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  return x;
+}
+
+// Lane i of each row of 16 lanes receives lane i + n's x (0 past the row's end).
+__device__ __forceinline__ float from_lane_above(float x, int n) {
+  const int v = __float_as_int(x);
+  switch (n) {
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x101, 0xF, 0xF, true));  // row_shl:1
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x102, 0xF, 0xF, true));  // row_shl:2
+    case 4: return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, true));  // row_shl:4
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x108, 0xF, 0xF, true));  // row_shl:8
+  }
+}
+
 // One workgroup checks every sequence's counts and stores the error word
 // (smallest bad sequence) with a plain store: no reset is needed before a call.
 __device__ void check_all(const ChainArgs& a) {
@@ -226,14 +247,12 @@ __global__ void __launch_bounds__(kThr, 8) k_chain_step(const ChainArgs a) {
     const int nt = min(kTileP, L - j0);
     stage_path<E, DK>(a, s, h, v0, rows, hl, j0, nt, sK, sV, sG);
     __syncthreads();
-    if (tid < 64) {  // inclusive suffix sums of the tile's log gates over the first kTileP lanes
+    static_assert(kTileP == 16, "the suffix scan runs over one row of 16 lanes");
+    if (tid < 64) {  // inclusive suffix sums of the tile's log gates over lanes 0..15
       const float gv = tid < nt ? sG[tid] : 0.f;
       float x = gv;
 #pragma unroll
-      for (int o = 1; o < kTileP; o <<= 1) {
-        const float y = __shfl_down(x, o);
-        if (tid + o < kTileP) x += y;
-      }
+      for (int o = 1; o < kTileP; o <<= 1) x += from_lane_above(x, o);
       if (tid < nt) sW[tid] = __expf(x - gv);
       if (tid == 0) sW[kTileP] = __expf(x);
     }
@@ -271,9 +290,7 @@ __global__ void __launch_bounds__(kThr, 8) k_chain_step(const ChainArgs a) {
     float u = 0.f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) u += S[i] * kt[8 * (i & ~3) + (i & 3)];
-    u += __shfl_xor(u, 1);
-    u += __shfl_xor(u, 2);
-    u += __shfl_xor(u, 4);
+    u = row_sum8(u);
     const float al = __expf(dG[t]);
     const float vt = dB[t] * (dV[t * kRows + r] - al * u);
     float o = 0.f;
@@ -283,9 +300,7 @@ __global__ void __launch_bounds__(kThr, 8) k_chain_step(const ChainArgs a) {
       S[i] = al * S[i] + vt * kt[c];
       o += S[i] * qt[c];
     }
-    o += __shfl_xor(o, 1);
-    o += __shfl_xor(o, 2);
-    o += __shfl_xor(o, 4);
+    o = row_sum8(o);
     if (cq == 0 && row_ok) {
       const size_t ro = (((size_t)s * N + t) * H + h) * Dv + v0 + r;
       og[ro] = (E)o;
