@@ -3,7 +3,7 @@ against the speculative chain-round oracle (oracle/chain.py).
 
 Eight rounds of chain drafts per sequence, with seeded accepted counts
 (including rounds that accept nothing and rounds that accept the whole draft),
-with drafts of 4 tokens and of 12.
+with drafts of 4, 7, 12 and 32 tokens and d_v of 16 to 128 (also unlike d_k).
 Every round's outputs and pseudo-values, and the committed state it starts from
 (state_out), are compared with the oracle: with the state written every round
 (history capacity 0), with a short history that flushes every few rounds, and
@@ -23,8 +23,8 @@ from gpu_helpers import record_margin, rel_l2, say
 pytestmark = pytest.mark.gpu
 
 
-def _draft(rng, n_seq, N, H, D, dtype):
-    q, k, v, beta, g = W._values(rng, n_seq * N, H, D, D, dtype)
+def _draft(rng, n_seq, N, H, D, dtype, Dv=None):
+    q, k, v, beta, g = W._values(rng, n_seq * N, H, D, D if Dv is None else Dv, dtype)
     sh = lambda a: a.reshape((n_seq, N) + a.shape[1:])
     return {"q": sh(q), "k": sh(k), "v": sh(v), "beta": sh(beta), "log_gate": sh(g)}
 
@@ -42,6 +42,14 @@ def test_chain_rounds_long_drafts(dtype, D, cap):
     _rounds_against_oracle(dtype, D, cap, n_seq=4, N=12, H=2, R=5, seed=200 + cap + D, tag="n12_")
 
 
+@pytest.mark.parametrize("dtype,D,Dv,cap,N", [("bf16", 128, 80, 40, 32), ("f32", 32, 48, 0, 7), ("bf16", 64, 16, 9, 3)])
+def test_chain_rounds_ragged_dv_and_longest_draft(dtype, D, Dv, cap, N):
+    """d_v of 80, 48 and 16 (a last block of 16 rows of S), the longest draft
+    (32 tokens) with a 40-token history (paths of up to 72 tokens, five tiles
+    with a ragged last one), and a 7-token draft without history."""
+    _rounds_against_oracle(dtype, D, cap, n_seq=3, N=N, H=2, R=5, seed=400 + cap + Dv, tag="dv_", Dv=Dv)
+
+
 @pytest.mark.parametrize("cap", [0, 16])
 def test_chain_rounds_full_size(cap):
     """The benched size: 64 sequences x 32 heads x d 128, 4-token drafts, bf16,
@@ -51,12 +59,13 @@ def test_chain_rounds_full_size(cap):
     _rounds_against_oracle("bf16", 128, cap, n_seq=64, N=4, H=32, R=3, seed=300 + cap, tag="full_")
 
 
-def _rounds_against_oracle(dtype, D, cap, n_seq, N, H, R, seed, tag):
+def _rounds_against_oracle(dtype, D, cap, n_seq, N, H, R, seed, tag, Dv=None):
     from tree_forked_gated_amd import binding as B
     rng = np.random.default_rng(seed)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    S0 = W._init(rng, n_seq, H, D, D, True)
-    rounds = [_draft(rng, n_seq, N, H, D, dtype) for _ in range(R)]
+    Dv = D if Dv is None else Dv
+    S0 = W._init(rng, n_seq, H, Dv, D, True)
+    rounds = [_draft(rng, n_seq, N, H, D, dtype, Dv) for _ in range(R)]
     acc = [rng.integers(0, N + 1, n_seq) for _ in range(R)]
     if R >= 4:  # a round that accepts nothing and one that accepts every draft
         acc[2][:] = 0
@@ -68,7 +77,7 @@ def _rounds_against_oracle(dtype, D, cap, n_seq, N, H, R, seed, tag):
     ref, S_end = chain_rounds(S0, rounds, acc)
     cr = B.ChainRounds(torch.from_numpy(S0).cuda(), N, cap, tdt, keep_state=True)
     tol = 1e-2 if dtype == "bf16" else 1e-4
-    say(f"chain rounds {dtype} D={D} hist_cap={cap}: {n_seq} sequences x {R} rounds of {N} draft tokens")
+    say(f"chain rounds {dtype} Dk={D} Dv={Dv} hist_cap={cap}: {n_seq} sequences x {R} rounds of {N} draft tokens")
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(tdt).contiguous()
     worst = {"out": 0.0, "pseudo_v": 0.0, "state": 0.0}
     for r in range(R + 1):
@@ -88,7 +97,7 @@ def _rounds_against_oracle(dtype, D, cap, n_seq, N, H, R, seed, tag):
     # the forced flush leaves the committed state in the checkpoint and an empty history
     ck = rel_l2(cr.ckpt.cpu().numpy(), S_end)
     say(f"  worst rel-L2 over the rounds {worst}; checkpoint after the flush {ck:.2e}")
-    record_margin(f"chain/{tag}{dtype}_d{D}_cap{cap}", tol=tol, checkpoint=ck, **worst)
+    record_margin(f"chain/{tag}{dtype}_d{D}_dv{Dv}_cap{cap}", tol=tol, checkpoint=ck, **worst)
     assert ck <= tol
     assert int(cr.hist_len[1 - cr.cur].abs().sum()) == 0
 
