@@ -6,7 +6,8 @@ softmax state, probabilities rounded to bf16 for the value product), plus a
 per-row bound of 5e-2 of the typical row norm. Cases: sequences of 1, 63, 64,
 65, 127, 128 and 129 tokens (tile boundaries), an empty sequence, forks from
 the last and first token of a tile and from mid-tile tokens, nested forks, draft
-trees (tree chunks), grouped key/value heads; at full size the decision-round
+trees (tree chunks), groups of 1 to 12 query heads per key/value head (every
+kernel shape, with and without cached keys); at full size the decision-round
 structure and the mixed forest with sampled rows; bitwise request isolation; plan reuse; the level
 capacity error.
 """
@@ -79,7 +80,7 @@ def _compare(name, got, ref):
     assert e <= 1e-2 and worst <= ROW_TOL, (name, e, worst)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (8, 1)])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (8, 1), (12, 1), (6, 1)])
 def test_tile_boundaries_forks_and_trees(Hq, Hkv):
     parent, seq = _stream([1, 63, 64, 0, 65, 127, 128, 129, 300],
                           forks=[(8, 63, 40), (8, 64, 70), (7, 127, 3), (6, 126, 65), (8, 200, 90), (8, 0, 5),
@@ -189,14 +190,16 @@ def test_level_capacity_is_reported():
     assert bool((out == 3.0).all())  # nothing computed
 
 
-def test_cached_keys_resume_a_request():
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (8, 1), (3, 1)])
+def test_cached_keys_resume_a_request(Hq, Hkv):
     """Flide section 3.4: a request resumed with cached keys and values of its
     checkpoint matches the fresh request (the cached part as real prefix
     tokens) and the oracle; sequences without cached rows and draft trees over
-    cached rows share the stream; a bad cache_start is refused on the device."""
+    cached rows share the stream; a bad cache_start is refused on the device.
+    Groups of 2, 8 and 3 query heads per key/value head run the kernel's three
+    shapes (four waves of two heads, eight waves, four waves of one head)."""
     from tree_forked_gated_amd import binding as B
     rng = np.random.default_rng(16)
-    Hq, Hkv = 4, 2
     pa, sa = _stream([150], forks=[(0, 100, 40), (0, 149, 20)])
     pb, sb = _stream([70], drafts=[30])  # a chain and a draft tree
     na, nb = pa.shape[0], pb.shape[0]
@@ -214,7 +217,7 @@ def test_cached_keys_resume_a_request():
     torch.cuda.synchronize()
     ref = fork_attention(q, k, v, parent, seq, 0.125, k_cache=kc, v_cache=vc, cache_start=cache_start)
     say(f"attention with cached keys: T={T}, cached rows {C0} + {C2}")
-    _compare("cached_keys", out.float().cpu().numpy(), ref)
+    _compare(f"cached_keys_h{Hq}_{Hkv}", out.float().cpu().numpy(), ref)
     # the fresh request: sequence 0's cached rows as a chain prefix that its roots hang off
     fp = np.concatenate([np.arange(-1, C0 - 1), np.where(pa < 0, C0 - 1, pa + C0)]).astype(np.int32)
     fresh, _ = B.attention(f(np.concatenate([np.zeros((C0, Hq, 128), np.float32), q[:na]])),
@@ -231,7 +234,7 @@ def test_cached_keys_resume_a_request():
                           k_cache=f(kc[:45]), v_cache=f(vc[:45]), cache_start=cs2, check=True)
     torch.cuda.synchronize()
     ref2 = fork_attention(q, k, v, parent, seq, 0.125, k_cache=kc[:45], v_cache=vc[:45], cache_start=cs2)
-    _compare("cached_keys_replanned", out2.float().cpu().numpy(), ref2)
+    _compare(f"cached_keys_replanned_h{Hq}_{Hkv}", out2.float().cpu().numpy(), ref2)
     with pytest.raises(B.GdnDeviceError) as ei:
         B.attention(f(q), f(k), f(v), parent, seq, scale=0.125, max_levels=lv, workspace=ws, planned=True,
                     k_cache=f(kc[:45]), v_cache=f(vc[:45]), cache_start=np.array([0, 30, 20, 45], np.int32),
