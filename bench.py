@@ -99,25 +99,31 @@ def _code_only(text):
     return "\n".join(ln for ln in lines if ln)
 
 
-def source_digest():
-    """Digest of what defines the walk kernel's code: its sources without
-    their comments and the compiler flags it is built with (its traffic does
-    not depend on the metadata or commit kernels, nor on a comment)."""
+def kernel_digest(src):
+    """Digest of what defines the code of one kernel source file: the file and
+    csrc/gdn_internal.h without their comments, and the compiler flags the file
+    is built with (a kernel's traffic does not depend on the other kernels, nor
+    on a comment)."""
     from tree_forked_gated_amd import build as hipbuild
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "tree_forked_gated_amd")
-    for name in ("csrc/gdn_internal.h", "csrc/walk_pipe.hip"):
+    for name in ("csrc/gdn_internal.h", f"csrc/{src}"):
         h.update(_code_only(open(os.path.join(pkg, name)).read()).encode())
-    flags = [f for f in hipbuild.FLAGS if not f.startswith(ROOT)] + hipbuild.FILE_FLAGS.get("walk_pipe.hip", [])
+    flags = [f for f in hipbuild.FLAGS if not f.startswith(ROOT)] + hipbuild.FILE_FLAGS.get(src, [])
     h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload_name):
-    """HBM bytes of one forward's walk (all its level launches) from the
-    committed rocprofv3 counter summary, or None when there is none or the
-    kernels changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"walk_traffic_{workload_name}.md")
+def source_digest():
+    """Digest of the walk kernel's code (walk_pipe.hip)."""
+    return kernel_digest("walk_pipe.hip")
+
+
+def profile_value(fname, src, key, profiles_dir=None):
+    """A figure (`- key: value` line) of a committed rocprofv3 counter summary
+    under profiles/, or None when there is none or the kernel source `src`
+    changed since the counters were taken (the summary's source_digest)."""
+    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"), fname)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -125,12 +131,18 @@ def measured_traffic(workload_name):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             kv[k.strip()] = v.strip().strip("`")
-    if kv.get("source_digest") != source_digest():
+    if kv.get("source_digest") != kernel_digest(src):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
+
+
+def measured_traffic(workload_name):
+    """HBM bytes of one forward's walk (all its level launches) from the
+    committed counter summary of that workload, or None."""
+    return profile_value(f"walk_traffic_{workload_name}.md", "walk_pipe.hip", "hbm_bytes_per_launch")
 
 
 # ------------------------------------------------------------------------ main
@@ -577,7 +589,9 @@ def attention_main(args):
     tf = cnt["flops"] / (ms_kern * 1e-3) / 1e12
     log(f"attention: {ms_step:.4f} ms/step, kernel {ms_kern:.4f} ms ({tf:.1f} TFLOP/s)")
     roof = {"bound": "mfma", "achieved": round(tf, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "k_fork_attn",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "traffic": profile_value(f"attention_traffic_{name}.md", "attention.hip", "hbm_bytes_per_call"),
+            "kernel": "k_fork_attn",
             "launch_unit": "one attention call (metadata reused)", "ms_per_step": round(ms_kern, 5),
             "alg_flops": cnt["flops"], "alg_bytes": cnt["bytes"]}
     cpu = parity = None
@@ -624,6 +638,8 @@ def attention_main(args):
 # --------------------------------------------------------------- chain rounds
 
 CHAIN_METRIC = "speculative chain rounds: draft tokens verified per second on 1 MI355X; fraction of HBM roofline"
+# counter summary of k_chain_step on the benched rounds (HBM bytes per round, per history capacity)
+CHAIN_TRAFFIC = "chain_rounds_traffic_64x4_h32_d128.md"
 
 
 def chain_round_bytes(acc_rounds, N, H, Dk, Dv, cap, es=2):
@@ -715,11 +731,14 @@ def chain_main(args):
                        "heads": H, "d_k": D, "d_v": D, "history_capacity": best, "accepted": "uniform 0..4",
                        "parallelism": "single GPU"},
             "roofline": {"bound": "hbm", "achieved": round(d["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "k_chain_step",
+                         "frac": round(d["gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": profile_value(CHAIN_TRAFFIC, "chain.hip", f"hbm_bytes_per_round_cap{best}"),
+                         "kernel": "k_chain_step",
                          "launch_unit": "one round", "alg_bytes": d["bytes_per_round"]},
             "other_mode": {"history_capacity": other, "ms_per_round": round(results[other]["ms_per_round"], 5),
                            "bytes_per_round": results[other]["bytes_per_round"],
-                           "hbm_frac": round(results[other]["gbs"] / HBM_PEAK_GBS, 4)},
+                           "hbm_frac": round(results[other]["gbs"] / HBM_PEAK_GBS, 4),
+                           "traffic": profile_value(CHAIN_TRAFFIC, "chain.hip", f"hbm_bytes_per_round_cap{other}")},
             "cpu_baseline": cpu, "parity_vs_oracle": parity,
             "step_ms_percentiles": {"p10": round(float(np.percentile(d["per"], 10)), 5),
                                     "p50": round(float(np.median(d["per"])), 5),

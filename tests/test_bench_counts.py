@@ -61,3 +61,20 @@ def test_walk_digest_ignores_comments_only():
     assert bench._code_only(src.replace("// a note", "// another note\n\n")) == bench._code_only(src)
     assert bench._code_only(src.replace("a + 2", "a + 3")) != bench._code_only(src)
     assert len(bench.source_digest()) == 16
+
+
+def test_counter_summaries_are_keyed_by_their_kernel(tmp_path):
+    """A counter summary's figures are read only while its digest names the
+    current code of its own kernel file: the walk's key is the per-file digest
+    of walk_pipe.hip, a summary with another digest gives None, and one whose
+    digest matches gives its figure."""
+    import bench
+    assert bench.source_digest() == bench.kernel_digest("walk_pipe.hip")
+    assert len({bench.kernel_digest(f) for f in ("walk_pipe.hip", "chain.hip", "attention.hip")}) == 3
+    (tmp_path / "x.md").write_text(f"# x\n\n- source_digest: `{bench.kernel_digest('chain.hip')}`\n- bytes: 123\n")
+    (tmp_path / "y.md").write_text("# y\n\n- source_digest: `0000000000000000`\n- bytes: 123\n")
+    d = str(tmp_path)
+    assert bench.profile_value("x.md", "chain.hip", "bytes", d) == 123.0
+    assert bench.profile_value("x.md", "attention.hip", "bytes", d) is None
+    assert bench.profile_value("y.md", "chain.hip", "bytes", d) is None
+    assert bench.profile_value("missing.md", "chain.hip", "bytes", d) is None
