@@ -8,8 +8,9 @@ Every round's outputs and pseudo-values, and the committed state it starts from
 (state_out), are compared with the oracle: with the state written every round
 (history capacity 0), with a short history that flushes every few rounds, and
 with a history long enough that nothing flushes until a forced flush. After
-the forced flush the checkpoint itself must hold the committed state. A bad
-accepted count is reported on the device and its sequence skipped.
+the forced flush the checkpoint itself must hold the committed state. Rounds
+replayed from captured graphs equal eager rounds bit for bit. A bad accepted
+count is reported on the device and its sequence skipped.
 """
 import numpy as np
 import pytest
@@ -100,6 +101,59 @@ def _rounds_against_oracle(dtype, D, cap, n_seq, N, H, R, seed, tag, Dv=None):
     record_margin(f"chain/{tag}{dtype}_d{D}_dv{Dv}_cap{cap}", tol=tol, checkpoint=ck, **worst)
     assert ck <= tol
     assert int(cr.hist_len[1 - cr.cur].abs().sum()) == 0
+
+
+@pytest.mark.parametrize("cap", [0, 6])
+def test_chain_rounds_replayed_from_graphs(cap):
+    """TreeWY section 4: a chain round is one graph-capturable kernel, since the
+    accepted counts and history lengths are device data. Two graphs are
+    captured, one per parity of the alternating buffers, and replayed for eight
+    rounds with new drafts and accepted counts copied into their static inputs
+    (eager work and host synchronisation between replays); every round's
+    outputs, pseudo-values and starting state equal an eager run's bit for bit
+    and match the oracle. With capacity 6 the same two graphs append to the
+    history in some rounds and flush it in others."""
+    from tree_forked_gated_amd import binding as B
+    rng = np.random.default_rng(500 + cap)
+    n_seq, N, H, D, R = 8, 4, 4, 128, 8
+    S0 = W._init(rng, n_seq, H, D, D, True)
+    rounds = [_draft(rng, n_seq, N, H, D, "bf16") for _ in range(R)]
+    acc = [rng.integers(0, N + 1, n_seq) for _ in range(R)]
+    ref, _ = chain_rounds(S0, rounds, acc)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(torch.bfloat16).contiguous()
+    init = torch.from_numpy(S0).cuda()
+    cr_e = B.ChainRounds(init, N, cap, torch.bfloat16, keep_state=True)
+    cr_g = B.ChainRounds(init, N, cap, torch.bfloat16, keep_state=True)
+    stat = [{kk: f(x) for kk, x in rounds[0].items()} for _ in range(2)]  # static drafts, by parity
+    eager = [{kk: f(x) for kk, x in rounds[0].items()} for _ in range(2)]
+    a_g = torch.zeros(n_seq, dtype=torch.int32, device="cuda")
+    cr_g.prev_k, cr_g.prev_g = stat[1]["k"], stat[1]["log_gate"]
+    graphs = [torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()]
+    torch.cuda.synchronize()
+    for par in range(2):
+        with torch.cuda.graph(graphs[par]):
+            cr_g.step(stat[par], a_g)
+    assert cr_g.cur == 0
+    say(f"chain rounds from graphs, hist_cap={cap}: {n_seq} sequences x {R} rounds")
+    for r in range(R):
+        par = r % 2
+        prev_acc = np.zeros(n_seq, np.int32) if r == 0 else acc[r - 1].astype(np.int32)
+        for kk, x in rounds[r].items():
+            stat[par][kk].copy_(f(x))
+            eager[par][kk].copy_(f(x))
+        a_g.copy_(torch.from_numpy(prev_acc))
+        graphs[par].replay()
+        torch.cuda.synchronize()
+        out_g, pv_g, st_g = cr_g.out[par].clone(), cr_g.pv[par].clone(), cr_g.state.clone()
+        out_e, pv_e = cr_e.step(eager[par], torch.from_numpy(prev_acc).cuda(), check=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e) and torch.equal(pv_g, pv_e), f"round {r}: replay differs from eager"
+        assert torch.equal(st_g, cr_e.state), f"round {r}: starting state differs from eager"
+        e = rel_l2(out_g.float().cpu().numpy(), ref[r]["out"])
+        es = rel_l2(st_g.cpu().numpy(), ref[r]["start_state"])
+        assert e <= 1e-2 and es <= 1e-2, (r, e, es)
+    B.raise_device_error(cr_g.workspace)
+    assert all(torch.equal(x, y) for x, y in zip(cr_g.hist_len, cr_e.hist_len)) and torch.equal(cr_g.ckpt, cr_e.ckpt)
 
 
 def test_bad_accepted_count_is_reported():
