@@ -8,8 +8,8 @@ per-row bound of 5e-2 of the typical row norm. Cases: sequences of 1, 63, 64,
 the last and first token of a tile and from mid-tile tokens, nested forks, draft
 trees (tree chunks), groups of 1 to 12 query heads per key/value head (every
 kernel shape, with and without cached keys); at full size the decision-round
-structure and the mixed forest with sampled rows; bitwise request isolation; plan reuse; the level
-capacity error.
+structure and the mixed forest with sampled rows; bitwise request isolation; plan reuse; replay
+of one captured call for trees of the same sizes; the level capacity error.
 """
 import numpy as np
 import pytest
@@ -34,10 +34,11 @@ def _values(rng, T, Hq, Hkv, D=128):
     return W.bf16_round(q), W.bf16_round(k), W.bf16_round(v)
 
 
-def _stream(lens, forks=(), drafts=()):
+def _stream(lens, forks=(), drafts=(), seed=5):
     """Chains of the given lengths plus branches (sequence, local fork token,
-    length) appended to their sequence, then draft trees of the given sizes."""
-    rng = np.random.default_rng(5)
+    length) appended to their sequence, then draft trees of the given sizes
+    (drawn with the seed)."""
+    rng = np.random.default_rng(seed)
     parents, starts, used = [], [0], 0
     for s, L in enumerate(lens):
         par = list(range(-1, L - 1)) if L else []
@@ -174,6 +175,50 @@ def test_request_isolation_bitwise_and_plan_reuse():
         B.attention(f(qa), f(ka), f(va), pa, sa, scale=0.1, max_levels=_levels(parent, seq),
                     workspace=ws, planned=True, check=True)
     assert ei.value.code == 8
+
+
+def test_attention_replayed_from_a_graph():
+    """Flide section 3.3: the span lists and items are built on the GPU and the
+    launch shapes depend only on the sizes, so one captured call (its metadata
+    rebuilt inside the graph) serves every tree of those sizes. Replayed for
+    four trees of equal size (forks from the first, middle and last token of a
+    trunk, and a different draft tree each time), with their structure and
+    values copied into the graph's static inputs and eager calls and host
+    synchronisation between replays: every replay equals the eager call bit for
+    bit and matches the oracle."""
+    from tree_forked_gated_amd import binding as B
+    Hq, Hkv = 16, 2
+    trees = [_stream([200, 120], forks=[(1, fp, 80)], drafts=[30], seed=60 + i) for i, fp in enumerate((50, 119, 0, 64))]
+    T = trees[0][0].shape[0]
+    assert all(p.shape[0] == T and np.array_equal(sq, trees[0][1]) for p, sq in trees)
+    lv = max(_levels(p, sq) for p, sq in trees)
+    rng = np.random.default_rng(61)
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda().to(torch.bfloat16)
+    vals = [_values(rng, T, Hq, Hkv) for _ in trees]
+    sq_d = torch.from_numpy(trees[0][1]).cuda()
+    par_d = torch.from_numpy(trees[0][0]).cuda()
+    q_d, k_d, v_d = f(vals[0][0]), f(vals[0][1]), f(vals[0][2])
+    out_d, ws = B.attention(q_d, k_d, v_d, par_d, sq_d, max_levels=lv, scale=0.1, check=True)  # sets the kernel up
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        B.attention(q_d, k_d, v_d, par_d, sq_d, max_levels=lv, scale=0.1, workspace=ws, out=out_d)
+    say(f"attention from a graph: T={T} Hq={Hq} Hkv={Hkv}, {len(trees)} trees")
+    for i in (1, 2, 0, 3):
+        (parent, seq), (q, k, v) = trees[i], vals[i]
+        par_d.copy_(torch.from_numpy(parent))
+        q_d.copy_(f(q))
+        k_d.copy_(f(k))
+        v_d.copy_(f(v))
+        out_d.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        B.raise_device_error(ws)
+        got = out_d.clone()
+        ref_e, _ = B.attention(f(q), f(k), f(v), parent, seq, max_levels=lv, scale=0.1, check=True)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref_e), f"tree {i}: replay differs from the eager call"
+        _compare(f"graph_tree{i}", got.float().cpu().numpy(), fork_attention(q, k, v, parent, seq, 0.1))
 
 
 def test_level_capacity_is_reported():
