@@ -12,13 +12,13 @@ HEADER = os.path.join(ROOT, "include", "gdn_tree.h")
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gdn_tree_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(gdn_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_boundary():
     names = _declared()
     for n in ["gdn_tree_forward", "gdn_tree_commit", "gdn_tree_workspace_size", "gdn_tree_check_error",
-              "gdn_tree_strerror", "gdn_tree_plan"]:
+              "gdn_tree_strerror", "gdn_tree_plan", "gdn_tree_attention", "gdn_chain_step", "gdn_tree_forward_static"]:
         assert n in names
 
 
@@ -147,3 +147,72 @@ def test_attention_argument_errors_need_no_gpu():
     a.flags = 0
     a.scale = float("nan")
     assert B.lib.gdn_tree_attention(ctypes.byref(a), None) == -6
+
+
+def test_commit_argument_errors_need_no_gpu():
+    """gdn_tree_commit refuses bad arguments on the host, before anything is
+    enqueued: sizes, a negative path count, missing pointers and workspace,
+    and states, keys or pseudo-values that are not 16-byte aligned."""
+    from tree_forked_gated_amd import binding as B
+    assert B.lib.gdn_tree_commit(None, None) == -1
+    a = B.CommitArgs()
+    a.dims = B.make_dims(100, 2, 48, 32, 1, B.GDN_BF16, 0, 1)
+    assert B.lib.gdn_tree_commit(ctypes.byref(a), None) == -2  # d_k 48
+    a.dims = B.make_dims(100, 2, 64, 32, 1, B.GDN_BF16, 0, 1)
+    a.n_path = -1
+    assert B.lib.gdn_tree_commit(ctypes.byref(a), None) == -6
+    a.n_path = 3
+    assert B.lib.gdn_tree_commit(ctypes.byref(a), None) == -1  # no workspace
+    a.workspace = ctypes.c_void_p(4096)
+    a.workspace_bytes = 4
+    assert B.lib.gdn_tree_commit(ctypes.byref(a), None) == -4
+    a.workspace_bytes = int(B.lib.gdn_tree_commit_workspace_size())
+    assert B.lib.gdn_tree_commit(ctypes.byref(a), None) == -1  # k, paths, ... missing
+    for f in ["k", "log_gate", "parent_idx", "seq_start", "init_state", "pseudo_v", "path_ptr", "path_nodes",
+              "path_seq", "out_state"]:
+        setattr(a, f, ctypes.c_void_p(8192))
+    for f in ["out_state", "init_state", "k", "pseudo_v"]:
+        setattr(a, f, ctypes.c_void_p(8200))
+        assert B.lib.gdn_tree_commit(ctypes.byref(a), None) == -6, f
+        assert b"aligned" in B.lib.gdn_tree_last_error()
+        setattr(a, f, ctypes.c_void_p(8192))
+
+
+def test_chain_argument_errors_need_no_gpu():
+    """gdn_chain_step refuses bad arguments on the host, before anything is
+    enqueued: sizes, missing buffers, buffers that must differ, misaligned
+    rows, a too small workspace and unknown flags."""
+    from tree_forked_gated_amd import binding as B
+    assert B.lib.gdn_chain_step(None, None) == -1
+    a = B.ChainArgs()
+    for kw, code in [(dict(dtype=7), -3), (dict(N=0), -2), (dict(N=33), -2), (dict(Dk=16), -2), (dict(Dv=24), -2),
+                     (dict(hist_cap=-1), -2)]:
+        base = dict(n_seq=2, N=4, H=2, Dk=64, Dv=32, dtype=B.GDN_BF16, hist_cap=4)
+        base.update(kw)
+        a.dims = B.ChainDims(base["n_seq"], base["N"], base["H"], base["Dk"], base["Dv"], base["dtype"],
+                             base["hist_cap"])
+        assert B.lib.gdn_chain_step(ctypes.byref(a), None) == code, kw
+    a.dims = B.ChainDims(2, 4, 2, 64, 32, B.GDN_BF16, 4)
+    assert B.lib.gdn_chain_step(ctypes.byref(a), None) == -1  # buffers missing
+    ptrs = ["ckpt", "hist_len_in", "hist_len_out", "prev_pv", "prev_k", "prev_g", "accepted", "q", "k", "v",
+            "log_gate", "beta", "out", "pseudo_v", "workspace"]
+    for i, f in enumerate(ptrs):
+        setattr(a, f, ctypes.c_void_p(4096 * (i + 1)))
+    assert B.lib.gdn_chain_step(ctypes.byref(a), None) == -1  # a history capacity needs the history buffers
+    for i, f in enumerate(["hist_pv", "hist_k", "hist_g"]):
+        setattr(a, f, ctypes.c_void_p(4096 * (len(ptrs) + i + 1)))
+    a.hist_len_out = a.hist_len_in
+    assert B.lib.gdn_chain_step(ctypes.byref(a), None) == -6
+    a.hist_len_out = ctypes.c_void_p(4096 * 40)
+    a.pseudo_v = a.prev_pv
+    assert B.lib.gdn_chain_step(ctypes.byref(a), None) == -6
+    a.pseudo_v = ctypes.c_void_p(4096 * 41)
+    a.ckpt = ctypes.c_void_p(4096 + 8)
+    assert B.lib.gdn_chain_step(ctypes.byref(a), None) == -6
+    assert b"aligned" in B.lib.gdn_tree_last_error()
+    a.ckpt = ctypes.c_void_p(4096)
+    a.workspace_bytes = 4
+    assert B.lib.gdn_chain_step(ctypes.byref(a), None) == -4
+    a.workspace_bytes = 8
+    a.flags = 4
+    assert B.lib.gdn_chain_step(ctypes.byref(a), None) == -6  # unknown flag
