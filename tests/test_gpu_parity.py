@@ -10,7 +10,7 @@ import pytest
 
 from tree_forked_gated_amd import workloads as W
 
-from gpu_helpers import f64, oracle_ref, record_margin, rel_l2, run_forward, say, tol
+from gpu_helpers import f64, oracle_ref, record_margin, rel_l2, run_forward, say, to_device, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +49,39 @@ def test_random_fp32(seed, Dk, Dv):
 def test_random_bf16(seed, Dk, Dv):
     wl = W.random_small(seed, n_seq=4, H=2, Dk=Dk, Dv=Dv, dtype="bf16", max_len=300)
     _check(wl, f"random_bf16[{seed}]")
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv,seed", [("f32", 64, 48, 21), ("bf16", 128, 128, 22), ("bf16", 64, 32, 23)])
+def test_degenerate_gates_and_betas(dtype, Dk, Dv, seed):
+    """The extremes the recurrence admits, mixed into a random stream: log
+    gates of 0 (no decay) and of -40 (the state all but cleared: alpha =
+    4e-18), and beta of 0 (the token writes nothing) and of 1 (a full
+    replacement along its key). Forward outputs, leaf states and pseudo-values,
+    and the commit of every sequence's deepest path, against the oracle."""
+    import oracle
+    import torch
+    from tree_forked_gated_amd import binding as B
+    wl = W.random_small(seed, n_seq=4, H=2, Dk=Dk, Dv=Dv, dtype=dtype, max_len=300)
+    rng = np.random.default_rng(seed)
+    pick = rng.random(wl.log_gate.shape)
+    wl.log_gate = np.where(pick < 0.15, 0.0, np.where(pick < 0.25, -40.0, wl.log_gate)).astype(np.float32)
+    pick = rng.random(wl.beta.shape)
+    wl.beta = np.where(pick < 0.15, 0.0, np.where(pick < 0.3, 1.0, wl.beta)).astype(np.float32)
+    res, ref = _check(wl, f"degenerate_{dtype}[{seed}]")
+    ptr, nodes = [0], []
+    for s_ in range(wl.n_seq):
+        a, b = int(wl.seq_start[s_]), int(wl.seq_start[s_ + 1])
+        deepest = max((W.root_path(wl.parent, t) for t in range(a, b)), key=len, default=[])
+        nodes += deepest
+        ptr.append(len(nodes))
+    ptr, nodes, seqs = np.array(ptr, np.int32), np.array(nodes, np.int32), np.arange(wl.n_seq, dtype=np.int32)
+    d = to_device(wl)
+    got = B.commit(d["k"], d["log_gate"], d["parent_idx"], d["seq_start"], d["init_state"], res.pseudo_v, ptr, nodes,
+                   seqs, check=True)
+    torch.cuda.synchronize()
+    e = rel_l2(f64(got), oracle.commit(wl, "f64", path_ptr=ptr, path_nodes=nodes, path_seq=seqs))
+    say(f"  commit rel-L2 {e:.3e}")
+    assert e <= tol(wl), e
 
 
 def test_chains_bf16():
