@@ -14,7 +14,8 @@ sequence, node indices outside [0, T), a path whose sequence index is out of
 range each raise the path error with the
 smallest bad path's index, both when one workgroup decides the error word (up
 to 1024 paths) and when the workgroups raise it by atomics (more paths); the
-states of the good paths are still written and still match the oracle.
+states of the good paths are still written and still match the oracle. Zero paths
+enqueue nothing but the error word's reset.
 """
 import numpy as np
 import pytest
@@ -167,3 +168,15 @@ def test_commit_bad_paths_raise_smallest(n_lead):
     e = rel_l2(f64(got)[ok_rows], ref)
     say(f"  error {ei.value.code} at {ei.value.index}; good paths rel-L2 {e:.3e}")
     assert e <= tol(wl), e
+
+
+def test_commit_of_no_paths():
+    """Zero paths: nothing is computed, the error word reads no error."""
+    from tree_forked_gated_amd import binding as B
+    wl = _workload(41, "bf16", 64, 32)
+    res, d = run_forward(wl, keep_pseudo=True, state_rows=W.leaves_of(wl.parent))
+    ws = torch.full((int(B.lib.gdn_tree_commit_workspace_size()),), 255, dtype=torch.uint8, device="cuda")
+    got = _commit(d, res, np.zeros(1, np.int32), np.zeros(0, np.int32), np.zeros(0, np.int32), check=False,
+                  workspace=ws)
+    assert got.shape[0] == 0
+    B.raise_device_error(ws)
