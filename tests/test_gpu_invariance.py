@@ -9,6 +9,9 @@ same bits as the branch run as a sequence of its own whose initial state is
 that fork state (read back through a state row at the fork token). Branches
 here are longer than one chunk so that both runs cut them into the same
 64-token chunks from the branch's first token.
+
+Repeated calls: the forward, ForkAttention and the commit, run again on the
+same inputs into outputs prefilled with NaN or 7, give the same bits.
 """
 import numpy as np
 import pytest
@@ -115,3 +118,47 @@ def test_branch_in_stream_equals_branch_alone(dtype, D):
         assert np.array_equal(_bits(rx.out[sl]), _bits(ra.out)), i
         assert np.array_equal(_bits(rx.pseudo_v[sl]), _bits(ra.pseudo_v)), i
         start += bl
+
+
+def test_repeated_calls_are_bitwise_equal():
+    """Races or reads of unwritten memory would show as differences between
+    repeated calls on the same inputs. The forward over a nested-forest stream
+    (several fork levels, items claimed dynamically), planned and not,
+    ForkAttention over the same stream, and the commit of draft-tree paths each
+    run again into outputs prefilled with NaN and with 7, and agree with the
+    first call bit for bit."""
+    from gpu_helpers import to_device
+    from tree_forked_gated_amd import binding as B
+    wl = W.mixed_forest(seed=91, total=12000, H=8, D=128)
+    d = to_device(wl)
+    rows = W.leaves_of(wl.parent)
+    cap = B.capacities(wl.parent, wl.seq_start)
+    args = (d["q"], d["k"], d["v"], d["log_gate"], d["beta"], d["parent_idx"], d["seq_start"], d["init_state"])
+    kw = dict(state_rows=rows, keep_pseudo=True, max_forks=cap["max_forks"], max_levels=cap["max_levels"])
+    first = B.forward(*args, check=True, **kw)
+    kq, vq = d["k"][:, :2].contiguous(), d["v"][:, :2].contiguous()
+    att0, aws = B.attention(d["q"], kq, vq, d["parent_idx"], d["seq_start"], max_levels=cap["max_levels"], check=True)
+    dt = W.draft_trees(seed=92, n_seq=16, n_nodes=64, H=8, D=128)
+    dd = to_device(dt)
+    cres = B.forward(dd["q"], dd["k"], dd["v"], dd["log_gate"], dd["beta"], dd["parent_idx"], dd["seq_start"],
+                     dd["init_state"], state_rows=np.zeros(0, np.int32), keep_pseudo=True, check=True,
+                     **B.capacities(dt.parent, dt.seq_start))
+    cargs = (dd["k"], dd["log_gate"], dd["parent_idx"], dd["seq_start"], dd["init_state"], cres.pseudo_v,
+             dt.path_ptr, dt.path_nodes, dt.path_seq)
+    com0 = B.commit(*cargs, check=True)
+    torch.cuda.synchronize()
+    say(f"repeat runs: forest T={wl.T} ({cap['max_levels']} levels), draft trees {dt.n_path} paths")
+    for fill, planned in ((float("nan"), False), (7.0, True), (float("nan"), True)):
+        out, st, pv = (torch.full_like(x, fill) for x in (first.out, first.state, first.pseudo_v))
+        B.forward(*args, out=out, state_out=st, pseudo_v=pv, workspace=first.workspace, planned=planned, check=True,
+                  **kw)
+        att = torch.full_like(att0, fill)
+        B.attention(d["q"], kq, vq, d["parent_idx"], d["seq_start"], max_levels=cap["max_levels"], workspace=aws,
+                    out=att, planned=planned, check=True)
+        com = torch.full_like(com0, fill)
+        B.commit(*cargs, out_state=com, check=True)
+        torch.cuda.synchronize()
+        assert torch.equal(out, first.out) and torch.equal(st, first.state) and torch.equal(pv, first.pseudo_v), \
+            (fill, planned, "forward")
+        assert torch.equal(att, att0), (fill, planned, "attention")
+        assert torch.equal(com, com0), (fill, planned, "commit")
