@@ -201,7 +201,7 @@ def test_attention_replayed_from_a_graph():
     out_d, ws = B.attention(q_d, k_d, v_d, par_d, sq_d, max_levels=lv, scale=0.1, check=True)  # sets the kernel up
     g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
-    with torch.cuda.graph(g):
+    with B.capture_guard(), torch.cuda.graph(g):
         B.attention(q_d, k_d, v_d, par_d, sq_d, max_levels=lv, scale=0.1, workspace=ws, out=out_d)
     say(f"attention from a graph: T={T} Hq={Hq} Hkv={Hkv}, {len(trees)} trees")
     for i in (1, 2, 0, 3):

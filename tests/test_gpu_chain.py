@@ -131,7 +131,7 @@ def test_chain_rounds_replayed_from_graphs(cap):
     graphs = [torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()]
     torch.cuda.synchronize()
     for par in range(2):
-        with torch.cuda.graph(graphs[par]):
+        with B.capture_guard(), torch.cuda.graph(graphs[par]):
             cr_g.step(stat[par], a_g)
     assert cr_g.cur == 0
     say(f"chain rounds from graphs, hist_cap={cap}: {n_seq} sequences x {R} rounds")

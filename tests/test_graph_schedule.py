@@ -61,3 +61,40 @@ def test_spare_rows_are_distinct_and_unused():
     assert sorted(rows.tolist()) == [3, 4, 5, 6, 7]
     rows = GraphFamily._spare_rows(3, np.array([0, 1]), 10, 6)
     assert rows.tolist() == [6, 7, 8]
+
+
+def test_capture_guard_collects_first_and_keeps_the_collector_off():
+    """A graph capture runs with Python's cyclic collector off, after one
+    collection: a dead cycle is finalised before the capture, never inside it,
+    and the collector's state is restored afterwards (also after an error)."""
+    import gc
+
+    from tree_forked_gated_amd import binding as B
+    finalised = []
+
+    class Holder:
+        def __del__(self):
+            finalised.append(gc.isenabled())
+
+    a, b = Holder(), Holder()
+    a.other, b.other = b, a  # a dead cycle once the names go
+    del a, b
+    assert gc.isenabled()
+    with B.capture_guard():
+        assert finalised == [True, True]  # collected at entry, before the body
+        assert not gc.isenabled()
+        c, d = Holder(), Holder()
+        c.other, d.other = d, c
+        del c, d
+        for _ in range(2000):  # enough allocations to trip an automatic collection
+            [object() for _ in range(10)]
+        assert len(finalised) == 2
+    assert gc.isenabled()
+    gc.collect()
+    assert len(finalised) == 4
+    try:
+        with B.capture_guard():
+            raise ValueError("inside")
+    except ValueError:
+        pass
+    assert gc.isenabled()

@@ -7,7 +7,9 @@ fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import gc
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -528,6 +530,23 @@ def commit(k, log_gate, parent_idx, seq_start, init_state, pseudo_v, path_ptr, p
 
 # -------------------------------------------------------------- graph replay
 
+@contextlib.contextmanager
+def capture_guard():
+    """Python's cyclic garbage collector runs before a graph capture and stays
+    off during it. A dead reference cycle that holds device tensors or graphs
+    (an exception's traceback kept by a caller, say) would otherwise be
+    finalised whenever the collector happens to run, and freeing or destroying
+    device objects while a stream captures aborts the process."""
+    gc.collect()
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if was:
+            gc.enable()
+
+
 class ForwardGraph:
     """One captured forward (and optionally one commit) per size bucket,
     replayed for any tree that fits the bucket.
@@ -625,7 +644,7 @@ class ForwardGraph:
         torch.cuda.current_stream(self.device).wait_stream(s)
         torch.cuda.synchronize(self.device)
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+        with capture_guard(), torch.cuda.graph(g):
             self._launch()
         self.graph = g
         return self
